@@ -1,0 +1,219 @@
+/*
+ * dwdp.h -- C ABI of the one-rank DWDP MoE block for AMD Instinct MI355X (gfx950).
+ *
+ * DWDP (Distributed Weight Data Parallelism; paper summary "DWDP: Distributed
+ * Weight Data Parallelism for High-Performance LLM Inference on NVL72") keeps
+ * every rank data-parallel, leaves each rank a resident share of every MoE
+ * layer's experts, and pulls the missing experts of layer l+1 into the other
+ * half of a double buffer while layer l runs (§2 Methodology Overview).  The
+ * expert GEMM reads the resident and the prefetched buffers directly instead of
+ * merging them first (§4.2), and the pulls are cut into fixed-size slices
+ * issued round-robin (§4.3.2).  This library is that rank's hot path:
+ *
+ *   dwdp_route_topk       router GEMM, top-k selection, renormalised softmax weights
+ *   dwdp_permute          expert histogram, prefix scan, stable scatter, row gather
+ *                         (with per-token fp8 quantisation when asked)
+ *   dwdp_moe_grouped_ffn  grouped SwiGLU expert FFN over a per-expert pointer table
+ *   dwdp_combine          weighted unpermute + shared expert
+ *   dwdp_prefetch_chunks  chunked round-robin copy of the next layer's experts
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are plain device addresses; the caller allocates and owns
+ *     every buffer, stream and event.  The library allocates no device memory
+ *     and keeps no pointer after a call returns.
+ *   - `stream` arguments are hipStream_t values (NULL = the legacy default
+ *     stream); `event` arguments are hipEvent_t values.
+ *   - Calls are asynchronous and stream ordered; the caller keeps every buffer
+ *     alive until the enqueued work has finished.
+ *   - Arguments are validated before anything is enqueued; on error nothing is
+ *     launched, a DWDP_ERR_* code is returned and dwdp_last_error() describes it.
+ *   - T == 0 (no tokens) is a valid no-op.
+ *   - Results are bitwise deterministic for identical inputs and do not depend
+ *     on which buffer or slot an expert's weights sit in.
+ *   - Device-side index values outside their range (a topk_idx entry outside
+ *     [0, E)) are not diagnosed; kernels stay in bounds and drop such entries.
+ *
+ * Layouts (row-major, C order)
+ *   x          [T, H]            tokens, bf16 (f32 for the f32 path)
+ *   w_router   [E, H]            router weight, same dtype as x
+ *   expert e   W13 [2I, H]       gate rows 0..I-1, then up rows (Wg stacked on Wu)
+ *              W2  [H, I]        down projection
+ *              fp8 only: S13 [2I/128, H/128] and S2 [H/128, I/128] fp32 block
+ *              scales, one per 128x128 block of W13 / W2 ([out, in] blocks)
+ *   x_perm     [rows, H]         rows = T*k + shared*T: routed rows ordered by
+ *                                expert and, inside an expert, by t*k+j; then
+ *                                the T shared-expert rows in token order
+ *   offsets    [E+shared+1]      group g owns x_perm rows [offsets[g], offsets[g+1])
+ *   y_perm     [rows, H]         expert outputs in x_perm's row order
+ */
+#ifndef DWDP_H_
+#define DWDP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DWDP_OK = 0,
+    DWDP_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, bad dtype combination */
+    DWDP_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+    DWDP_ERR_WORKSPACE = 3,     /* workspace smaller than dwdp_workspace_bytes() */
+    DWDP_ERR_HIP = 4            /* a HIP runtime call failed (message in dwdp_last_error) */
+} dwdp_status;
+
+typedef enum {
+    DWDP_F32 = 0,               /* IEEE binary32 */
+    DWDP_BF16 = 1,              /* bfloat16 */
+    DWDP_FP8_E4M3 = 2           /* OCP FP8 E4M3 ("FN": no infinities, 448 max), fp32 scales */
+} dwdp_dtype;
+
+typedef enum {
+    DWDP_OP_PERMUTE = 0,
+    DWDP_OP_GROUPED_FFN = 1
+} dwdp_op;
+
+typedef enum {
+    DWDP_COPY_HIPMEMCPY = 0,    /* one hipMemcpyAsync per slice, slices issued round-robin */
+    DWDP_COPY_KERNEL = 1        /* one launch of the library's slice-copy kernel walking the same plan */
+} dwdp_copy_engine;
+
+/* One entry of the per-expert pointer table (the split-weight "TensorList",
+ * paper summary §4.2): where group g's weights live.  s13/s2 are NULL unless
+ * the weights are fp8.  Any entry may point into any buffer; two entries may
+ * point at the same weights (redundant placement, §2). */
+typedef struct {
+    const void* w13;
+    const void* w2;
+    const float* s13;
+    const float* s2;
+} dwdp_expert_ptrs;
+
+/* One prefetch source: `bytes` bytes at device address `src` go to dst + dst_offset. */
+typedef struct {
+    const void* src;
+    size_t dst_offset;
+    size_t bytes;
+} dwdp_copy_src;
+
+/* One slice of a prefetch plan, in issue order. */
+typedef struct {
+    int32_t source;
+    int32_t pad_;
+    size_t src_offset;
+    size_t dst_offset;
+    size_t bytes;
+} dwdp_chunk;
+
+/* Router: logits = x * w_router^T + bias (fp32 accumulation; bf16 inputs are
+ * multiplied exactly), then per token the k largest logits (equal logits: the
+ * lower expert index first; slots ordered by logit descending) and their
+ * weights softmax(logits of the chosen k).  The pages give no gate formula;
+ * this softmax top-k gate with renormalisation over the chosen k is the
+ * reading taken.
+ *   x [T,H], w_router [E,H]: DWDP_F32 or DWDP_BF16 (in_dtype), 16-byte aligned.
+ *   bias [E] fp32 or NULL.   1 <= k <= E <= 1024, k <= 32, H % 8 == 0.
+ *   logits_out [T,E] fp32, topk_idx [T,k] int32, topk_w [T,k] fp32. */
+int dwdp_route_topk(const void* x, const void* w_router, int in_dtype, const float* bias,
+                    int64_t T, int H, int E, int k,
+                    float* logits_out, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Permutation by expert (counting sort, stable in t*k+j) and row gather.
+ *   topk_idx [T,k] int32.  shared in {0,1}.
+ *   x [T,H] of x_dtype (F32 or BF16).  act_dtype == x_dtype copies rows bitwise;
+ *   act_dtype == DWDP_FP8_E4M3 (x_dtype BF16, H % 128 == 0) quantises each row
+ *   per 128-column group: scale = amax/448 (1 when amax is 0), code =
+ *   E4M3(value/scale) rounded to nearest even, saturating; x_perm then holds
+ *   codes (uint8) and x_perm_scale [rows, H/128] the scales.
+ *   Outputs: x_perm [rows,H], offsets [E+shared+1], perm_src [rows] (source token
+ *   of each row), inv_perm [T,k] (row of each (t,j)).
+ *   ws: dwdp_workspace_bytes(DWDP_OP_PERMUTE, ...) bytes of device scratch. */
+int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, int shared,
+                 const void* x, int x_dtype, int act_dtype, int H,
+                 void* x_perm, float* x_perm_scale,
+                 int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped SwiGLU FFN, reading each group's weights through `table` (device
+ * array of n_groups entries) -- no merge of the split buffers (paper summary §4.2).
+ *   For group g and its rows X = x_perm[offsets[g]:offsets[g+1]]:
+ *     A = silu(X W13[0:I]^T) * (X W13[I:2I]^T),   y_perm rows = A W2^T
+ *   w_dtype F32: x_perm, weights and y_perm fp32, fp32 math.
+ *   w_dtype BF16: x_perm and weights bf16, fp32 accumulation, A rounded to bf16,
+ *     y_perm bf16.
+ *   w_dtype FP8_E4M3: x_perm codes + x_perm_scale (see dwdp_permute), weights
+ *     codes + 128x128 block scales; products accumulated in fp32 per 128-wide K
+ *     block and scaled by (row scale * block scale); A quantised per row and
+ *     128-column group like x; y_perm bf16.
+ *   rows must equal offsets[n_groups] (not checked on the device).  H % 128 == 0,
+ *   I % 128 == 0 (BF16/FP8); H % 4, I % 4 == 0 (F32).  offsets is read on the
+ *   device only; no host synchronisation happens.
+ *   ws: dwdp_workspace_bytes(DWDP_OP_GROUPED_FFN, ...) bytes (holds A). */
+int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,
+                         const void* x_perm, const float* x_perm_scale, int64_t rows, int H, int I,
+                         int w_dtype, void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Combine: y[t] = sum_{j<k} topk_w[t,j] * y_perm[inv_perm[t,j]] (+ y_perm[T*k + t]
+ * when shared), summed in fp32 in slot order then the shared row, rounded once
+ * to out_dtype.  y_perm is fp32 for out_dtype F32, bf16 otherwise. */
+int dwdp_combine(const void* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T, int k,
+                 int shared, int H, int out_dtype, void* y, void* stream);
+
+/* Layer-ahead prefetch (paper summary §2 and §4.3.2): copy every source into
+ * dst + dst_offset, cut into chunk_bytes slices issued round-robin over the
+ * sources (slice c of every source before slice c+1 of any; the last slice of
+ * a source may be short).  Destination ranges must not overlap.
+ *   srcs: host array of n_src entries (1 <= n_src <= 64).
+ *   engine: DWDP_COPY_HIPMEMCPY or DWDP_COPY_KERNEL; max_workgroups bounds the
+ *   kernel engine's grid (0 = 32) and is ignored by the other engine.
+ *   wait_event (nullable): copy_stream waits on it first (the last reader of the
+ *   destination slots).  done_event (nullable): recorded on copy_stream after
+ *   the last slice. */
+int dwdp_prefetch_chunks(void* dst, const dwdp_copy_src* srcs, int n_src, size_t chunk_bytes,
+                         int engine, int max_workgroups,
+                         void* copy_stream, void* wait_event, void* done_event);
+
+/* Host only: the slice plan dwdp_prefetch_chunks issues, in issue order.  Writes
+ * at most max_chunks entries to out (out may be NULL to count) and the total
+ * number of slices to *n_chunks. */
+int dwdp_prefetch_plan(const dwdp_copy_src* srcs, int n_src, size_t chunk_bytes,
+                       dwdp_chunk* out, size_t max_chunks, size_t* n_chunks);
+
+/* Host only: fill a host pointer table from a placement.  Group g's record
+ * starts at buffers[buf_of[g]] + slot_of[g] * record_bytes, laid out as
+ * [W13 | W2 | S13 | S2] with every part 256-byte aligned (S13/S2 for fp8 only).
+ * The caller uploads `out` (n_groups entries) to device memory. */
+int dwdp_fill_expert_table(void* const* buffers, int n_buffers, const int32_t* buf_of,
+                           const int32_t* slot_of, int n_groups, int H, int I, int w_dtype,
+                           dwdp_expert_ptrs* out);
+
+/* Host only: bytes of one expert record in the layout above. */
+size_t dwdp_expert_record_bytes(int H, int I, int w_dtype);
+
+/* Byte offsets of W2, S13 and S2 inside an expert record. */
+int dwdp_expert_record_offsets(int H, int I, int w_dtype, size_t* off_w2, size_t* off_s13,
+                               size_t* off_s2);
+
+/* Block-quantise a weight matrix w [rows, cols] (fp32) to E4M3 codes q [rows, cols]
+ * and fp32 scales s [rows/128, cols/128]: per 128x128 block, scale = amax/448
+ * (1 when amax is 0) and code = E4M3(w/scale).  rows, cols multiples of 128. */
+int dwdp_quantize_weight_fp8(const float* w, int64_t rows, int64_t cols, uint8_t* q, float* s,
+                             void* stream);
+
+/* Device scratch the given operation needs (0 when none). */
+size_t dwdp_workspace_bytes(int op, int64_t T, int k, int E, int H, int I, int dtype, int shared);
+
+/* Description of the last error on the calling thread ("" if none).  Valid
+ * until the next dwdp_* call on the same thread. */
+const char* dwdp_last_error(void);
+
+/* Library version string. */
+const char* dwdp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DWDP_H_ */

@@ -1,0 +1,686 @@
+// Grouped expert GEMMs of the MoE block and the router GEMM, for gfx950.
+//
+// The split-weight grouped GEMM of the DWDP paper summary (§4.2) reads each
+// expert's weights wherever they sit -- the resident partition or a prefetch
+// slot -- through a per-group pointer table, instead of first merging the
+// buffers with a device-to-device copy.  Here that table is an array of
+// dwdp_expert_ptrs in device memory, read once per workgroup tile.
+//
+// Structure
+//   * A tile schedule is built on the device from the group row offsets (no
+//     host round trip): every group is cut into BM-row m-tiles; tile `lin`
+//     of the (group, n-tile, m-tile) order -- m fastest, so the m-tiles that
+//     share one weight tile run back to back -- is found from lin / NT.
+//   * Workgroup ids are remapped so that each of the 8 XCDs (one 4 MB L2
+//     each) walks one contiguous stretch of that order: the m-tiles sharing a
+//     weight tile and the n-tiles sharing an activation tile are resident in
+//     the same L2 at the same time, so HBM sees each weight byte about once.
+//   * bf16 / fp8: both operands are K-contiguous; 128-byte row slices are
+//     staged through LDS (XOR-swizzled 16-byte chunks, double buffered,
+//     global loads for step k+1 in flight during the MFMAs of step k) and fed
+//     to v_mfma_f32_32x32x16_bf16 or v_mfma_scale_f32_32x32x64_f8f6f4 (unit
+//     scales).  fp8 keeps a per-128-K partial sum and folds it into the fp32
+//     accumulator with (row scale x block scale).
+//   * GEMM1's weight tile holds the gate rows and the up rows of the same
+//     output columns, so SwiGLU is applied in registers in the epilogue.
+//   * f32 (small shapes only): LDS-tiled FMA kernel with the same schedule.
+#include "common.h"
+#include "internal.h"
+
+namespace dwdp {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum Kind { kGemm1 = 0, kGemm2 = 1, kRouter = 2 };
+
+struct MTile {
+    int32_t g;    // group
+    int32_t m0;   // index of the group's first m-tile
+    int32_t mc;   // the group's m-tile count
+    int32_t pad;
+};
+
+struct GemmParams {
+    const uint8_t* a;               // activation rows [rows, K]
+    const float* a_scale;           // fp8: [rows, K/128]
+    const dwdp_expert_ptrs* table;  // GEMM1 / GEMM2: per-group weights
+    const uint8_t* b_single;        // router: weight [N, K]
+    const float* bias;              // router: bias [N] or null
+    const int32_t* offsets;         // [G+1]
+    const int32_t* mprefix;         // [G+1]; mprefix[G] = number of m-tiles
+    const MTile* mtiles;            // one entry per m-tile
+    int64_t rows;                   // router: T
+    int G;
+    int N;                          // GEMM1: I (A columns); GEMM2: H; router: E
+    int K;
+    int NT;                         // n-tiles
+    int I;                          // GEMM1: first up row inside W13
+    uint8_t* out;
+    float* out_scale;               // GEMM1 fp8: A scales [rows, I/128]
+};
+
+struct Tile {
+    int g;
+    int nt;
+    int64_t row0;
+    int nrows;
+};
+
+template <int BM, int KIND>
+__device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
+    int total;
+    int mt_router = 0;
+    if (KIND == kRouter) {
+        mt_router = (int)((p.rows + BM - 1) / BM);
+        total = mt_router * p.NT;
+    } else {
+        total = p.mprefix[p.G] * p.NT;
+    }
+    const int per = (total + kNumXcd - 1) / kNumXcd;
+    const int bid = blockIdx.x;
+    const int slot = bid / kNumXcd;
+    if (slot >= per) return false;
+    const int lin = (bid % kNumXcd) * per + slot;
+    if (lin >= total) return false;
+    if (KIND == kRouter) {
+        const int mi = lin % mt_router;
+        t.g = 0;
+        t.nt = lin / mt_router;
+        t.row0 = (int64_t)mi * BM;
+        t.nrows = (int)min((int64_t)BM, p.rows - t.row0);
+        return true;
+    }
+    const MTile m = p.mtiles[lin / p.NT];
+    const int rem = lin - m.m0 * p.NT;
+    t.g = m.g;
+    t.nt = rem / m.mc;
+    const int mi = rem - t.nt * m.mc;
+    const int r0 = p.offsets[m.g], r1 = p.offsets[m.g + 1];
+    t.row0 = (int64_t)r0 + (int64_t)mi * BM;
+    t.nrows = min(BM, r1 - (int)t.row0);
+    return true;
+}
+
+// ------------------------------------------------------------------------------ schedule
+// One workgroup: m-tile counts per group, their exclusive scan, and the m-tile table.
+template <int BM>
+__global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int G,
+                                                        int32_t* __restrict__ mprefix, MTile* __restrict__ mtiles) {
+    __shared__ int wave_sum[16];
+    __shared__ int carry_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int base = 0; base < G; base += 1024) {
+        const int g = base + tid;
+        int c = 0;
+        if (g < G) {
+            const int n = offsets[g + 1] - offsets[g];
+            c = n > 0 ? (n + BM - 1) / BM : 0;
+        }
+        int incl = c;
+        for (int d = 1; d < 64; d <<= 1) {
+            int v = __shfl_up(incl, d);
+            if (lane >= d) incl += v;
+        }
+        if (lane == 63) wave_sum[wave] = incl;
+        __syncthreads();
+        int before = carry_s;
+        for (int w = 0; w < wave; ++w) before += wave_sum[w];
+        const int excl = before + incl - c;
+        if (g < G) {
+            mprefix[g] = excl;
+            for (int m = 0; m < c; ++m) mtiles[excl + m] = MTile{g, excl, c, 0};
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int s = 0;
+            for (int w = 0; w < 16; ++w) s += wave_sum[w];
+            carry_s += s;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) mprefix[G] = carry_s;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// ------------------------------------------------------------------------------ MFMA kernel
+// BM x BN tile, WM x WN waves, 128 bytes of K per step (64 bf16 or 128 fp8 elements).
+template <int BM, int BN, int WM, int WN, int KIND, bool FP8>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(GemmParams p) {
+    constexpr int NTHR = WM * WN * 64;
+    constexpr int ROWB = 128;
+    constexpr int KSTEP = FP8 ? 128 : 64;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int MI = TM / 32, NJ = TN / 32;
+    constexpr int AC = BM * 8 / NTHR, BC = BN * 8 / NTHR;
+    static_assert(AC >= 1 && BC >= 1 && BM * 8 % NTHR == 0 && BN * 8 % NTHR == 0, "tile / thread mismatch");
+    static_assert(KIND != kGemm1 || NJ % 2 == 0, "GEMM1 waves hold gate and up blocks in pairs");
+
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * ROWB];
+
+    Tile t;
+    if (!decode_tile<BM, KIND>(p, t)) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    const uint8_t* wbase;
+    const float* wscale = nullptr;
+    if (KIND == kGemm1) {
+        wbase = static_cast<const uint8_t*>(p.table[t.g].w13);
+        wscale = p.table[t.g].s13;
+    } else if (KIND == kGemm2) {
+        wbase = static_cast<const uint8_t*>(p.table[t.g].w2);
+        wscale = p.table[t.g].s2;
+    } else {
+        wbase = p.b_single;
+    }
+    const size_t ldk = (size_t)p.K * (FP8 ? 1 : 2);
+    const int KT = p.K / KSTEP;
+
+    // weight row held by tile row r
+    auto w_row = [&](int r) -> int {
+        if (KIND == kGemm1) {
+            constexpr int half = BN / 2;
+            const int n0 = t.nt * half;
+            return r < half ? n0 + r : p.I + n0 + (r - half);
+        }
+        return min(t.nt * BN + r, p.N - 1);
+    };
+    // tile row of the first row of the wave's n-block j
+    auto b_block_row = [&](int j) -> int {
+        if (KIND == kGemm1) {
+            constexpr int CW = BN / 2 / WN;
+            return j < NJ / 2 ? wn * CW + j * 32 : BN / 2 + wn * CW + (j - NJ / 2) * 32;
+        }
+        return wn * TN + j * 32;
+    };
+
+    const uint8_t* ga[AC];
+    int la[AC];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const int lin = tid + i * NTHR, r = lin >> 3, c = lin & 7;
+        const int rr = min(r, t.nrows - 1);
+        ga[i] = p.a + (size_t)(t.row0 + rr) * ldk + c * 16;
+        la[i] = r * ROWB + ((c ^ (r & 7)) << 4);
+    }
+    const uint8_t* gb[BC];
+    int lb[BC];
+#pragma unroll
+    for (int i = 0; i < BC; ++i) {
+        const int lin = tid + i * NTHR, r = lin >> 3, c = lin & 7;
+        gb[i] = wbase + (size_t)w_row(r) * ldk + c * 16;
+        lb[i] = r * ROWB + ((c ^ (r & 7)) << 4);
+    }
+
+    bool m_act[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) m_act[i] = wm * TM + i * 32 < t.nrows;
+
+    f32x16 acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    u32x4 ra[AC], rb[BC];
+    auto gload = [&](int kt) {
+        const size_t off = (size_t)kt * ROWB;
+#pragma unroll
+        for (int i = 0; i < AC; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ga[i] + off);
+#pragma unroll
+        for (int i = 0; i < BC; ++i) rb[i] = *reinterpret_cast<const u32x4*>(gb[i] + off);
+    };
+    auto sstore = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < AC; ++i) *reinterpret_cast<u32x4*>(&sA[st][la[i]]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < BC; ++i) *reinterpret_cast<u32x4*>(&sB[st][lb[i]]) = rb[i];
+    };
+    auto lds16 = [&](const uint8_t* s, int row, int chunk) -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(&s[row * ROWB + ((chunk ^ (row & 7)) << 4)]);
+    };
+
+    // fp8: per-row activation scales of this lane's accumulator rows
+    auto row_of = [&](int i, int r) -> int { return wm * TM + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3); };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) gload(kt + 1);
+        const uint8_t* A = sA[cur];
+        const uint8_t* B = sB[cur];
+        if constexpr (!FP8) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int ch = s * 2 + hi;
+                bf16x8 af[MI], bf[NJ];
+#pragma unroll
+                for (int i = 0; i < MI; ++i) af[i] = __builtin_bit_cast(bf16x8, lds16(A, wm * TM + i * 32 + l32, ch));
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) bf[j] = __builtin_bit_cast(bf16x8, lds16(B, b_block_row(j) + l32, ch));
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    if (!m_act[i]) continue;
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                }
+            }
+        } else {
+            f32x16 part[MI][NJ];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int ch = s * 4 + hi * 2;
+                i32x8 af[MI], bf[NJ];
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    const int row = wm * TM + i * 32 + l32;
+                    const u32x4 lo = lds16(A, row, ch), up = lds16(A, row, ch + 1);
+                    af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+                }
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int row = b_block_row(j) + l32;
+                    const u32x4 lo = lds16(B, row, ch), up = lds16(B, row, ch + 1);
+                    bf[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+                }
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    if (!m_act[i]) continue;
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+                        part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], part[i][j], 0, 0, 0, 127,
+                                                                                     0, 127);
+                }
+            }
+            // fold this 128-wide K block: acc += part * (row scale * block scale)
+            const int KB = p.K / kFp8Group;
+            float sb[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) sb[j] = wscale[(size_t)(w_row(b_block_row(j)) / kFp8Group) * KB + kt];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                if (!m_act[i]) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = min(row_of(i, r), t.nrows - 1);
+                    const float sa = p.a_scale[(size_t)(t.row0 + rr) * KB + kt];
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) acc[i][j][r] += part[i][j][r] * (sa * sb[j]);
+                }
+            }
+        }
+        if (kt + 1 < KT) sstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    if constexpr (KIND == kGemm1) {
+        constexpr int CW = BN / 2 / WN;          // A columns per wave
+        const int colA = t.nt * (BN / 2) + wn * CW;
+        if constexpr (!FP8) {
+            uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int jb = 0; jb < NJ / 2; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = row_of(i, r);
+                        if (m < t.nrows) {
+                            const float a = silu_mul(acc[i][jb][r], acc[i][jb + NJ / 2][r]);
+                            out[(size_t)(t.row0 + m) * p.N + colA + jb * 32 + l32] = f32_to_bf16(a);
+                        }
+                    }
+        } else {
+            // A is quantised per row and 128-column group; the tile spans exactly one group.
+            static_assert(!FP8 || KIND != kGemm1 || BN / 2 == kFp8Group, "fp8 GEMM1 tile must cover one A group");
+            __shared__ float red[WN][BM];
+            float av[MI][NJ / 2][16];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int jb = 0; jb < NJ / 2; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) av[i][jb][r] = silu_mul(acc[i][jb][r], acc[i][jb + NJ / 2][r]);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float m = 0.0f;
+#pragma unroll
+                    for (int jb = 0; jb < NJ / 2; ++jb) m = fmaxf(m, fabsf(av[i][jb][r]));
+#pragma unroll
+                    for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+                    if (l32 == 0) red[wn][row_of(i, r)] = m;
+                }
+            __syncthreads();
+            uint8_t* out = p.out;
+            const int IB = p.N / kFp8Group;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = row_of(i, r);
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w][m]);
+                    const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+                    if (m < t.nrows) {
+#pragma unroll
+                        for (int jb = 0; jb < NJ / 2; ++jb)
+                            out[(size_t)(t.row0 + m) * p.N + colA + jb * 32 + l32] = f32_to_e4m3(av[i][jb][r] / s);
+                        if (wn == 0 && l32 == 0) p.out_scale[(size_t)(t.row0 + m) * IB + t.nt] = s;
+                    }
+                }
+        }
+    } else if constexpr (KIND == kGemm2) {
+        uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = row_of(i, r);
+                    if (m < t.nrows)
+                        out[(size_t)(t.row0 + m) * p.N + t.nt * BN + wn * TN + j * 32 + l32] = f32_to_bf16(acc[i][j][r]);
+                }
+    } else {
+        float* out = reinterpret_cast<float*>(p.out);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int col = t.nt * BN + wn * TN + j * 32 + l32;
+            if (col >= p.N) continue;
+            const float b = p.bias ? p.bias[col] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = row_of(i, r);
+                    if (m < t.nrows) out[(size_t)(t.row0 + m) * p.N + col] = acc[i][j][r] + b;
+                }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ f32 kernel
+// 64 x 64 tile, 256 threads, 4 x 4 outputs per thread, K step 16.  Exact-ish
+// fp32 math (expf, IEEE division) for the small fp32 workload.
+template <int KIND>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
+    constexpr int BM = 64, BN = 64, BK = 16;
+    __shared__ float sA[BK][BM + 4];
+    __shared__ float sB[BK][BN + 4];
+    Tile t;
+    if (!decode_tile<BM, KIND>(p, t)) return;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const float* A = reinterpret_cast<const float*>(p.a);
+    const float* W;
+    if (KIND == kGemm1) W = static_cast<const float*>(p.table[t.g].w13);
+    else if (KIND == kGemm2) W = static_cast<const float*>(p.table[t.g].w2);
+    else W = reinterpret_cast<const float*>(p.b_single);
+    auto w_row = [&](int r) -> int {
+        if (KIND == kGemm1) {
+            const int n0 = t.nt * (BN / 2);
+            return r < BN / 2 ? n0 + r : p.I + n0 + (r - BN / 2);
+        }
+        return min(t.nt * BN + r, p.N - 1);
+    };
+    // my B tile rows: GEMM1 pairs gate rows tx*2,+1 with up rows 32+tx*2,+1; others tx*4..+3
+    int brow[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) brow[c] = KIND == kGemm1 ? (c < 2 ? tx * 2 + c : 32 + tx * 2 + (c - 2)) : tx * 4 + c;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < p.K; k0 += BK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int lin = tid + i * 256, r = lin >> 4, kk = lin & 15;
+            const int rr = min(r, t.nrows - 1);
+            sA[kk][r] = A[(size_t)(t.row0 + rr) * p.K + k0 + kk];
+            sB[kk][r] = W[(size_t)w_row(r) * p.K + k0 + kk];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = sA[kk][ty * 4 + i];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) b[c] = sB[kk][brow[c]];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[i][c] = fmaf(a[i], b[c], acc[i][c]);
+        }
+        __syncthreads();
+    }
+    float* out = reinterpret_cast<float*>(p.out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = ty * 4 + i;
+        if (m >= t.nrows) continue;
+        const size_t orow = (size_t)(t.row0 + m) * p.N;
+        if (KIND == kGemm1) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const float g = acc[i][c], u = acc[i][c + 2];
+                out[orow + t.nt * (BN / 2) + tx * 2 + c] = g / (1.0f + expf(-g)) * u;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int col = t.nt * BN + tx * 4 + c;
+                if (col < p.N) out[orow + col] = acc[i][c] + ((KIND == kRouter && p.bias) ? p.bias[col] : 0.0f);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ configs
+// bf16: 128 x 128 tiles, 2 x 2 waves.  fp8 GEMM1: 64 x 256 (one 128-column A
+// group per tile), 1 x 4 waves; fp8 GEMM2: 128 x 128.  Router: 64 x 64.
+constexpr int kBmBf16 = 128, kBnBf16 = 128;
+constexpr int kBmFp8G1 = 64, kBnFp8G1 = 256;
+constexpr int kBmFp8G2 = 128, kBnFp8G2 = 128;
+constexpr int kBmF32 = 64, kBnF32 = 64;
+constexpr int kBmRouter = 64, kBnRouter = 64;
+
+struct FfnShape {
+    int bm1, bn1, bm2, bn2;
+};
+
+FfnShape ffn_shape(int dtype) {
+    if (dtype == DWDP_BF16) return {kBmBf16, kBnBf16, kBmBf16, kBnBf16};
+    if (dtype == DWDP_FP8_E4M3) return {kBmFp8G1, kBnFp8G1, kBmFp8G2, kBnFp8G2};
+    return {kBmF32, kBnF32, kBmF32, kBnF32};
+}
+
+size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct FfnWs {
+    size_t a, a_scale, pre1, mt1, pre2, mt2, total;
+    int64_t maxm1, maxm2;
+};
+
+FfnWs ffn_ws_layout(int64_t rows, int groups, int I, int dtype) {
+    FfnShape s = ffn_shape(dtype);
+    FfnWs w{};
+    const size_t ea = dtype == DWDP_F32 ? 4 : dtype == DWDP_BF16 ? 2 : 1;
+    w.maxm1 = (rows + s.bm1 - 1) / s.bm1 + groups;
+    w.maxm2 = (rows + s.bm2 - 1) / s.bm2 + groups;
+    size_t off = 0;
+    w.a = off;
+    off += a256((size_t)rows * I * ea);
+    w.a_scale = off;
+    if (dtype == DWDP_FP8_E4M3) off += a256((size_t)rows * (I / kFp8Group) * 4);
+    w.pre1 = off;
+    off += a256((size_t)(groups + 1) * 4);
+    w.mt1 = off;
+    off += a256((size_t)w.maxm1 * sizeof(MTile));
+    w.pre2 = off;
+    off += a256((size_t)(groups + 1) * 4);
+    w.mt2 = off;
+    off += a256((size_t)w.maxm2 * sizeof(MTile));
+    w.total = off;
+    return w;
+}
+
+template <int BM>
+void launch_schedule(const int32_t* offsets, int G, int32_t* pre, MTile* mt, hipStream_t st) {
+    hipLaunchKernelGGL(schedule_kernel<BM>, dim3(1), dim3(1024), 0, st, offsets, G, pre, mt);
+}
+
+template <int BM, int BN, int WM, int WN, int KIND, bool FP8>
+void launch_mfma(const GemmParams& p, int64_t grid, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, KIND, FP8>), dim3((unsigned)grid), dim3(WM * WN * 64), 0, st, p);
+}
+
+template <int KIND>
+void launch_f32(const GemmParams& p, int64_t grid, hipStream_t st) {
+    hipLaunchKernelGGL(gemm_f32_kernel<KIND>, dim3((unsigned)grid), dim3(256), 0, st, p);
+}
+
+}  // namespace
+
+size_t ffn_ws_bytes(int64_t rows, int groups, int H, int I, int dtype) {
+    (void)H;
+    if (dtype != DWDP_F32 && dtype != DWDP_BF16 && dtype != DWDP_FP8_E4M3) return 0;
+    return ffn_ws_layout(rows, groups, I, dtype).total;
+}
+
+// Router GEMM: logits [T, E] = x [T, H] * w_router^T + bias.
+int router_gemm(const void* x, const void* w, int dtype, const float* bias, int64_t T, int H, int E, float* logits,
+                hipStream_t st) {
+    GemmParams p{};
+    p.a = static_cast<const uint8_t*>(x);
+    p.b_single = static_cast<const uint8_t*>(w);
+    p.bias = bias;
+    p.rows = T;
+    p.G = 1;
+    p.N = E;
+    p.K = H;
+    p.out = reinterpret_cast<uint8_t*>(logits);
+    if (dtype == DWDP_BF16) {
+        p.NT = (E + kBnRouter - 1) / kBnRouter;
+        const int64_t grid = ((T + kBmRouter - 1) / kBmRouter) * p.NT;
+        launch_mfma<kBmRouter, kBnRouter, 2, 2, kRouter, false>(p, grid, st);
+    } else {
+        p.NT = (E + kBnF32 - 1) / kBnF32;
+        const int64_t grid = ((T + kBmF32 - 1) / kBmF32) * p.NT;
+        launch_f32<kRouter>(p, grid, st);
+    }
+    DWDP_LAUNCHED();
+    return DWDP_OK;
+}
+
+}  // namespace dwdp
+
+using namespace dwdp;
+
+extern "C" int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,
+                                    const void* x_perm, const float* x_perm_scale, int64_t rows, int H, int I,
+                                    int w_dtype, void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    DWDP_REQUIRE(w_dtype == DWDP_F32 || w_dtype == DWDP_BF16 || w_dtype == DWDP_FP8_E4M3, "unknown w_dtype");
+    DWDP_REQUIRE(n_groups >= 1 && n_groups <= (1 << 20), "n_groups out of range");
+    DWDP_REQUIRE(rows >= 0 && rows < (int64_t)1 << 31, "rows out of range");
+    DWDP_REQUIRE(H > 0 && I > 0, "H and I must be positive");
+    if (w_dtype == DWDP_F32) {
+        DWDP_REQUIRE(H % 64 == 0 && I % 32 == 0 && H % 16 == 0 && I % 16 == 0, "f32 path needs H % 64 == 0, I % 32 == 0");
+    } else {
+        DWDP_REQUIRE(H % 128 == 0 && I % 128 == 0, "bf16/fp8 paths need H % 128 == 0 and I % 128 == 0");
+    }
+    if (rows == 0) return DWDP_OK;
+    DWDP_REQUIRE(table && offsets && x_perm && y_perm && ws, "null pointer argument");
+    DWDP_REQUIRE(aligned16(table) && aligned16(x_perm) && aligned16(y_perm) && aligned16(ws),
+                 "pointers must be 16-byte aligned");
+    if (w_dtype == DWDP_FP8_E4M3) DWDP_REQUIRE(x_perm_scale != nullptr, "fp8 needs x_perm_scale");
+    FfnWs L = ffn_ws_layout(rows, n_groups, I, w_dtype);
+    if (ws_bytes < L.total)
+        return fail(DWDP_ERR_WORKSPACE, "dwdp_moe_grouped_ffn: workspace too small (need " + std::to_string(L.total) + ")");
+    hipStream_t st = as_stream(stream);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    uint8_t* A = base + L.a;
+    float* As = reinterpret_cast<float*>(base + L.a_scale);
+    int32_t* pre1 = reinterpret_cast<int32_t*>(base + L.pre1);
+    MTile* mt1 = reinterpret_cast<MTile*>(base + L.mt1);
+    int32_t* pre2 = reinterpret_cast<int32_t*>(base + L.pre2);
+    MTile* mt2 = reinterpret_cast<MTile*>(base + L.mt2);
+    FfnShape s = ffn_shape(w_dtype);
+
+    GemmParams p1{};
+    p1.a = static_cast<const uint8_t*>(x_perm);
+    p1.a_scale = x_perm_scale;
+    p1.table = table;
+    p1.offsets = offsets;
+    p1.mprefix = pre1;
+    p1.mtiles = mt1;
+    p1.G = n_groups;
+    p1.N = I;
+    p1.K = H;
+    p1.I = I;
+    p1.NT = I / (s.bn1 / 2);
+    p1.out = A;
+    p1.out_scale = As;
+
+    GemmParams p2{};
+    p2.a = A;
+    p2.a_scale = As;
+    p2.table = table;
+    p2.offsets = offsets;
+    p2.G = n_groups;
+    p2.N = H;
+    p2.K = I;
+    p2.I = I;
+    p2.NT = H / s.bn2;
+    p2.out = static_cast<uint8_t*>(y_perm);
+
+    if (s.bm1 == s.bm2) {
+        p2.mprefix = pre1;
+        p2.mtiles = mt1;
+    } else {
+        p2.mprefix = pre2;
+        p2.mtiles = mt2;
+    }
+    const int64_t grid1 = L.maxm1 * p1.NT, grid2 = (s.bm1 == s.bm2 ? L.maxm1 : L.maxm2) * p2.NT;
+    DWDP_REQUIRE(grid1 < ((int64_t)1 << 31) && grid2 < ((int64_t)1 << 31), "problem too large for one launch");
+
+    if (w_dtype == DWDP_BF16) {
+        launch_schedule<kBmBf16>(offsets, n_groups, pre1, mt1, st);
+        launch_mfma<kBmBf16, kBnBf16, 2, 2, kGemm1, false>(p1, grid1, st);
+        launch_mfma<kBmBf16, kBnBf16, 2, 2, kGemm2, false>(p2, grid2, st);
+    } else if (w_dtype == DWDP_FP8_E4M3) {
+        launch_schedule<kBmFp8G1>(offsets, n_groups, pre1, mt1, st);
+        launch_schedule<kBmFp8G2>(offsets, n_groups, pre2, mt2, st);
+        launch_mfma<kBmFp8G1, kBnFp8G1, 1, 4, kGemm1, true>(p1, grid1, st);
+        launch_mfma<kBmFp8G2, kBnFp8G2, 2, 2, kGemm2, true>(p2, grid2, st);
+    } else {
+        launch_schedule<kBmF32>(offsets, n_groups, pre1, mt1, st);
+        launch_f32<kGemm1>(p1, grid1, st);
+        launch_f32<kGemm2>(p2, grid2, st);
+    }
+    DWDP_LAUNCHED();
+    return DWDP_OK;
+}

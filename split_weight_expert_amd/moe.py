@@ -1,0 +1,163 @@
+"""One DWDP rank's MoE block on top of the C ABI.
+
+ExpertStore holds a layer's expert records in separate device buffers -- the
+resident partition and a double-buffered prefetch area (DWDP paper summary,
+§2) -- and builds the per-group pointer table that the grouped GEMM reads
+instead of a merged copy (§4.2).  MoEBlock owns the activation buffers and
+workspaces for a token count and runs route -> permute -> grouped FFN ->
+combine on one stream.  Nothing here computes: every step is a libdwdp call.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import api
+from ._lib import BF16, F32, FP8_E4M3
+
+DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+_ACT_TORCH = {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.uint8}
+
+
+def act_dtype(w_dtype: int) -> torch.dtype:
+    """torch dtype of the tokens / block output (fp8 layers take bf16 tokens)."""
+    return torch.float32 if w_dtype == F32 else torch.bfloat16
+
+
+class ExpertStore:
+    """Expert records of one layer in `n_buffers` separate device allocations.
+
+    Buffer 0 is the resident partition; buffers 1.. are prefetch slot sets.
+    A record is [W13 | W2 | S13 | S2] (include/dwdp.h), `rec` bytes long.
+    """
+
+    def __init__(self, H: int, I: int, w_dtype: int, slots_per_buffer, device="cuda"):
+        self.H, self.I, self.w_dtype = H, I, w_dtype
+        self.rec = api.expert_record_bytes(H, I, w_dtype)
+        self.off_w2, self.off_s13, self.off_s2 = api.expert_record_offsets(H, I, w_dtype)
+        self.buffers = [torch.empty(max(n, 1) * self.rec, dtype=torch.uint8, device=device) for n in slots_per_buffer]
+        self.slots = list(slots_per_buffer)
+
+    def record(self, buf: int, slot: int) -> torch.Tensor:
+        assert 0 <= slot < self.slots[buf]
+        return self.buffers[buf][slot * self.rec:(slot + 1) * self.rec]
+
+    def record_ptr(self, buf: int, slot: int) -> int:
+        return self.buffers[buf].data_ptr() + slot * self.rec
+
+    def views(self, buf: int, slot: int):
+        """(W13, W2, S13, S2) tensor views of one record (S* are None unless fp8)."""
+        r = self.record(buf, slot)
+        H, I = self.H, self.I
+        dt = _ACT_TORCH[self.w_dtype]
+        eb = torch.tensor([], dtype=dt).element_size()
+        w13 = r[:2 * I * H * eb].view(dt).view(2 * I, H)
+        w2 = r[self.off_w2:self.off_w2 + H * I * eb].view(dt).view(H, I)
+        if self.w_dtype != FP8_E4M3:
+            return w13, w2, None, None
+        s13 = r[self.off_s13:self.off_s13 + (2 * I // 128) * (H // 128) * 4].view(torch.float32).view(2 * I // 128,
+                                                                                                     H // 128)
+        s2 = r[self.off_s2:self.off_s2 + (H // 128) * (I // 128) * 4].view(torch.float32).view(H // 128, I // 128)
+        return w13, w2, s13, s2
+
+    def load(self, buf: int, slot: int, wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tensor, stream=None):
+        """Place one expert's weights (device tensors; fp32 masters for fp8) into a record."""
+        w13, w2, s13, s2 = self.views(buf, slot)
+        if self.w_dtype == FP8_E4M3:
+            api.quantize_weight_fp8(torch.cat([wg, wu], 0).float().contiguous(), w13, s13, stream)
+            api.quantize_weight_fp8(wd.float().contiguous(), w2, s2, stream)
+        else:
+            w13[:self.I].copy_(wg)
+            w13[self.I:].copy_(wu)
+            w2.copy_(wd)
+
+    def table(self, placement, device="cuda") -> torch.Tensor:
+        """Device pointer table for placement = [(buffer, slot) for each group]."""
+        t = api.fill_expert_table([b.data_ptr() for b in self.buffers], [p[0] for p in placement],
+                                  [p[1] for p in placement], self.H, self.I, self.w_dtype)
+        return api.table_to_device(t, device)
+
+
+def dwdp_placement(E: int, n_local: int, shared: int, slot_set: int = 1):
+    """Experts [0, n_local) and the shared expert resident (buffer 0); the rest in prefetch slot set `slot_set`."""
+    pl = [(0, e) if e < n_local else (slot_set, e - n_local) for e in range(E)]
+    if shared:
+        pl.append((0, n_local))
+    return pl
+
+
+@dataclass
+class BlockBuffers:
+    logits: torch.Tensor
+    idx: torch.Tensor
+    w: torch.Tensor
+    x_perm: torch.Tensor
+    x_perm_scale: torch.Tensor | None
+    offsets: torch.Tensor
+    perm_src: torch.Tensor
+    inv_perm: torch.Tensor
+    y_perm: torch.Tensor
+    y: torch.Tensor
+    ws_perm: torch.Tensor
+    ws_ffn: torch.Tensor
+
+
+class MoEBlock:
+    """Route -> permute -> grouped SwiGLU FFN -> combine for one layer shape."""
+
+    def __init__(self, H: int, I: int, E: int, k: int, shared: int, dtype: str, device="cuda"):
+        self.H, self.I, self.E, self.k, self.shared = H, I, E, k, shared
+        self.w_dtype = DTYPES[dtype]
+        self.device = device
+        self._bufs: dict[int, BlockBuffers] = {}
+
+    def buffers(self, T: int) -> BlockBuffers:
+        if T in self._bufs:
+            return self._bufs[T]
+        H, I, E, k, S, dev = self.H, self.I, self.E, self.k, self.shared, self.device
+        rows = T * k + S * T
+        adt = act_dtype(self.w_dtype)
+        xp_dt = torch.uint8 if self.w_dtype == FP8_E4M3 else adt
+        ws_p = api.workspace_bytes(api.OP_PERMUTE, T, k, E, H, I, self.w_dtype, S)
+        ws_f = api.workspace_bytes(api.OP_GROUPED_FFN, T, k, E, H, I, self.w_dtype, S)
+        b = BlockBuffers(
+            logits=torch.empty(T, E, dtype=torch.float32, device=dev),
+            idx=torch.empty(T, k, dtype=torch.int32, device=dev),
+            w=torch.empty(T, k, dtype=torch.float32, device=dev),
+            x_perm=torch.empty(rows, H, dtype=xp_dt, device=dev),
+            x_perm_scale=(torch.empty(rows, H // 128, dtype=torch.float32, device=dev)
+                          if self.w_dtype == FP8_E4M3 else None),
+            offsets=torch.empty(E + S + 1, dtype=torch.int32, device=dev),
+            perm_src=torch.empty(rows, dtype=torch.int32, device=dev),
+            inv_perm=torch.empty(T, k, dtype=torch.int32, device=dev),
+            y_perm=torch.empty(rows, H, dtype=adt, device=dev),
+            y=torch.empty(T, H, dtype=adt, device=dev),
+            ws_perm=torch.empty(max(ws_p, 256), dtype=torch.uint8, device=dev),
+            ws_ffn=torch.empty(max(ws_f, 256), dtype=torch.uint8, device=dev),
+        )
+        self._bufs[T] = b
+        return b
+
+    def route(self, x, w_router, bias, b: BlockBuffers, stream=None):
+        api.route_topk(x, w_router, bias, self.k, b.logits, b.idx, b.w, stream)
+
+    def permute(self, x, b: BlockBuffers, stream=None):
+        api.permute(b.idx, self.E, self.shared, x, self.w_dtype if self.w_dtype == FP8_E4M3 else api.dtype_code(x),
+                    b.x_perm, b.x_perm_scale, b.offsets, b.perm_src, b.inv_perm, b.ws_perm, stream)
+
+    def ffn(self, table, b: BlockBuffers, stream=None):
+        api.moe_grouped_ffn(table, self.E + self.shared, b.offsets, b.x_perm, b.x_perm_scale, self.H, self.I,
+                            self.w_dtype, b.y_perm, b.ws_ffn, stream)
+
+    def combine(self, b: BlockBuffers, stream=None):
+        api.combine(b.y_perm, b.inv_perm, b.w, self.shared, b.y, stream)
+
+    def forward(self, x, w_router, bias, table, stream=None) -> BlockBuffers:
+        """The whole block on `stream`; results stay in the returned buffers."""
+        b = self.buffers(x.shape[0])
+        self.route(x, w_router, bias, b, stream)
+        self.permute(x, b, stream)
+        self.ffn(table, b, stream)
+        self.combine(b, stream)
+        return b

@@ -1,0 +1,150 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+rejects bad arguments before launching anything, and its host-only logic
+(slice plan, record layout, pointer table, workspace sizes) is right."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle.prefetch import chunk_plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dwdp.h")
+
+lib_mod = pytest.importorskip("split_weight_expert_amd._lib")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lib_mod.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dwdp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(lib_mod.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_version_and_empty_error(lib):
+    assert b"gfx950" in lib.dwdp_version()
+    assert lib.dwdp_last_error() == b""
+
+
+FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced: validation fails first
+ODD = ctypes.c_void_p(0x10004)
+
+
+def expect(code, rc, lib, needle):
+    assert rc == code, (rc, lib.dwdp_last_error())
+    assert needle in lib.dwdp_last_error().decode()
+
+
+def test_route_topk_rejects_bad_arguments(lib):
+    f = lib.dwdp_route_topk
+    E_ = lib_mod.DWDP_ERR_INVALID_ARG
+    expect(E_, f(FAKE, FAKE, 7, None, 4, 256, 8, 2, FAKE, FAKE, FAKE, None), lib, "in_dtype")
+    expect(E_, f(FAKE, FAKE, 0, None, 4, 256, 8, 9, FAKE, FAKE, FAKE, None), lib, "k must")
+    expect(E_, f(FAKE, FAKE, 0, None, 4, 256, 8, 0, FAKE, FAKE, FAKE, None), lib, "k must")
+    expect(E_, f(FAKE, FAKE, 1, None, 4, 100, 8, 2, FAKE, FAKE, FAKE, None), lib, "H % 64")
+    expect(E_, f(None, FAKE, 0, None, 4, 256, 8, 2, FAKE, FAKE, FAKE, None), lib, "null")
+    expect(E_, f(ODD, FAKE, 0, None, 4, 256, 8, 2, FAKE, FAKE, FAKE, None), lib, "aligned")
+    assert f(None, None, 0, None, 0, 256, 8, 2, None, None, None, None) == 0      # T = 0 is a no-op
+
+
+def test_permute_rejects_bad_arguments(lib):
+    f = lib.dwdp_permute
+    E_ = lib_mod.DWDP_ERR_INVALID_ARG
+    base = dict(idx=FAKE, T=4, k=2, E=8, S=0, x=FAKE, xd=1, ad=1, H=256, xp=FAKE, xs=None, off=FAKE, ps=FAKE,
+                ip=FAKE, ws=FAKE, wsb=1 << 20)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return f(a["idx"], a["T"], a["k"], a["E"], a["S"], a["x"], a["xd"], a["ad"], a["H"], a["xp"], a["xs"],
+                 a["off"], a["ps"], a["ip"], a["ws"], a["wsb"], None)
+    expect(E_, call(S=2), lib, "shared")
+    expect(E_, call(ad=2, xd=0), lib, "act_dtype")
+    expect(E_, call(ad=2, xs=None), lib, "x_perm_scale")
+    expect(E_, call(ad=2, H=200, xs=FAKE), lib, "H % 128")
+    expect(E_, call(xp=None), lib, "null")
+    expect(lib_mod.DWDP_ERR_WORKSPACE, call(wsb=16), lib, "workspace")
+
+
+def test_grouped_ffn_rejects_bad_arguments(lib):
+    f = lib.dwdp_moe_grouped_ffn
+    E_ = lib_mod.DWDP_ERR_INVALID_ARG
+    expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7168, 2048, 5, FAKE, FAKE, 1 << 30, None), lib, "w_dtype")
+    expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7000, 2048, 1, FAKE, FAKE, 1 << 30, None), lib, "H % 128")
+    expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7168, 2048, 2, FAKE, FAKE, 1 << 30, None), lib, "x_perm_scale")
+    expect(E_, f(FAKE, 9, FAKE, ODD, None, 128, 7168, 2048, 1, FAKE, FAKE, 1 << 30, None), lib, "aligned")
+    expect(lib_mod.DWDP_ERR_WORKSPACE, f(FAKE, 9, FAKE, FAKE, None, 128, 7168, 2048, 1, FAKE, FAKE, 64, None),
+           lib, "workspace")
+    assert f(None, 9, None, None, None, 0, 7168, 2048, 1, None, None, 0, None) == 0   # rows = 0
+
+
+def test_combine_and_prefetch_reject_bad_arguments(lib):
+    E_ = lib_mod.DWDP_ERR_INVALID_ARG
+    expect(E_, lib.dwdp_combine(FAKE, FAKE, FAKE, 4, 2, 0, 100, 1, FAKE, None), lib, "multiple of 8")
+    expect(E_, lib.dwdp_combine(FAKE, FAKE, FAKE, 4, 2, 3, 128, 1, FAKE, None), lib, "shared")
+    srcs = (lib_mod.CopySrc * 2)()
+    srcs[0].src, srcs[0].dst_offset, srcs[0].bytes = 0x10000, 0, 100
+    srcs[1].src, srcs[1].dst_offset, srcs[1].bytes = 0x20000, 50, 100
+    expect(E_, lib.dwdp_prefetch_chunks(FAKE, srcs, 2, 16, 0, 0, None, None, None), lib, "overlap")
+    srcs[1].dst_offset = 100
+    expect(E_, lib.dwdp_prefetch_chunks(FAKE, srcs, 2, 0, 0, 0, None, None, None), lib, "chunk_bytes")
+    expect(E_, lib.dwdp_prefetch_chunks(FAKE, srcs, 2, 16, 9, 0, None, None, None), lib, "engine")
+    expect(E_, lib.dwdp_prefetch_chunks(FAKE, srcs, 0, 16, 0, 0, None, None, None), lib, "n_src")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefetch_plan_matches_oracle(seed):
+    from split_weight_expert_amd import api
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 7))
+    sizes = [int(s) for s in rng.integers(0, 5000, size=n)]
+    chunk = int(rng.integers(1, 900))
+    offs = np.cumsum([0] + [s + 7 for s in sizes[:-1]]).tolist()
+    srcs = [(0x1000 * (i + 1), offs[i], sizes[i]) for i in range(n)]
+    got = api.prefetch_plan(srcs, chunk)
+    assert got == chunk_plan(sizes, offs, chunk)
+
+
+def test_prefetch_plan_for_the_fp8_overlap_workload():
+    from split_weight_expert_amd import api
+    rec = api.expert_record_bytes(7168, 2048, 2)
+    assert rec == 44_050_944
+    per = 64 * rec
+    plan = api.prefetch_plan([(0x1000, 0, per), (0x2000, per, per), (0x3000, 2 * per, per)], 4 << 20)
+    assert len(plan) == 3 * 673 and plan[-1][3] == 688_128
+    assert [p[0] for p in plan[:6]] == [0, 1, 2, 0, 1, 2]
+
+
+def test_record_layout_and_pointer_table():
+    from split_weight_expert_amd import api
+    assert api.expert_record_bytes(7168, 2048, 1) == 88_080_384
+    w2, s13, s2 = api.expert_record_offsets(7168, 2048, 2)
+    assert w2 == 2 * 2048 * 7168 and s13 == w2 + 7168 * 2048 and s2 == s13 + 1792 * 4
+    rec = api.expert_record_bytes(256, 128, 0)
+    t = api.fill_expert_table([0x100000, 0x900000], [0, 1, 1, 0], [0, 0, 3, 2], 256, 128, 0)
+    assert t[0].w13 == 0x100000 and t[1].w13 == 0x900000 and t[2].w13 == 0x900000 + 3 * rec
+    assert t[3].w2 == 0x100000 + 2 * rec + 2 * 128 * 256 * 4
+    assert t[0].s13 is None and t[0].s2 is None
+    with pytest.raises(lib_mod.DwdpError):
+        api.fill_expert_table([0x100000], [1], [0], 256, 128, 0)
+
+
+def test_workspace_sizes_grow_with_rows():
+    from split_weight_expert_amd import api
+    a = api.workspace_bytes(api.OP_GROUPED_FFN, 8192, 8, 256, 7168, 2048, 1, 1)
+    b = api.workspace_bytes(api.OP_GROUPED_FFN, 64, 8, 256, 7168, 2048, 1, 1)
+    assert a >= 73728 * 2048 * 2 and b >= 576 * 2048 * 2 and a > b
+    assert api.workspace_bytes(api.OP_PERMUTE, 8192, 8, 256, 7168, 2048, 1, 1) > 0

@@ -1,0 +1,405 @@
+"""Parity of every C-ABI entry point with the CPU oracle on the GPU.
+
+Small shapes that span several tiles and a ragged tail; the bars are
+bit-exact for routing indices, permutation and copies, and the stated
+tolerances for floating-point outputs (fp32 1e-5 max relative; bf16 2e-2
+max / 2e-3 mean; fp8 6e-2 max).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import codecs, moe as omoe
+from oracle.prefetch import apply_plan
+from synth.configs import shrink
+from tests.gpu_util import HostLayer, assert_close, need_gpu, rel_err, to_np, upload_layer
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def placement_split(cfg):
+    pl = [(0, e) if e < cfg.n_local else (1, e - cfg.n_local) for e in range(cfg.E)]
+    if cfg.shared:
+        pl.append((0, cfg.n_local))
+    return pl, [cfg.n_local + cfg.shared, cfg.E - cfg.n_local]
+
+
+# --------------------------------------------------------------------------------------- generator
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_gpu_generator_matches_host_generator(kind):
+    from synth import gen
+    key = gen.tensor_key(0, 5, 1, 3, 17)
+    n = 1_000_003
+    out = torch.empty(n, dtype=torch.float32 if kind == "f32" else torch.bfloat16, device=DEV)
+    gen.gpu_fill(key, n, 0.37, kind, out.data_ptr(), 0, first=12345)
+    torch.cuda.synchronize()
+    host = gen.host_fill(key, n, 0.37, kind, first=12345)
+    got = out.cpu().numpy() if kind == "f32" else out.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, host)
+
+
+# --------------------------------------------------------------------------------------- routing
+
+ROUTE_CASES = [
+    ("tiny_f32", dict()),
+    ("tiny_f32", dict(T=333, E=300, k=7)),          # E not a multiple of 64, ragged T
+    ("prefill8k_bf16", dict(T=257, H=1024, E=256, k=8)),
+    ("prefill8k_bf16", dict(T=1, H=7168, E=256, k=8)),
+    ("decode64_bf16", dict(T=64, H=7168, E=256, k=8)),
+    ("tiny_f32", dict(T=5, E=1, k=1)),
+    ("tiny_f32", dict(T=9, E=8, k=8)),              # k = E
+]
+
+
+@pytest.mark.parametrize("name,kw", ROUTE_CASES)
+def test_route_topk_parity(name, kw):
+    from split_weight_expert_amd import api
+    cfg = shrink(synth.get_config(name), **kw) if kw else synth.get_config(name)
+    x = synth.tokens(cfg)
+    wr = synth.router_weight(cfg)
+    b = synth.router_bias(cfg)
+    adt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    T, E, k = cfg.T, cfg.E, cfg.k
+    logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    api.route_topk(torch.from_numpy(x).to(DEV, adt), torch.from_numpy(wr).to(DEV, adt),
+                   None if b is None else torch.from_numpy(b).to(DEV), k, logits, idx, w)
+    torch.cuda.synchronize()
+    gl, gi, gw = logits.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    ref_l = omoe.router_logits(x, wr, b)
+    rms = np.sqrt((ref_l ** 2).mean())
+    assert np.abs(gl - ref_l).max() <= 1e-5 * rms
+    # bit-exact contract: the GPU's selection equals the oracle's selection on the GPU's logits
+    np.testing.assert_array_equal(gi, omoe.topk_select(gl, k))
+    np.testing.assert_allclose(gw, omoe.gate_weights(gl, gi), rtol=2e-6, atol=1e-7)
+    # and the oracle's own routing differs only where its k-th / (k+1)-th margin is below 1e-4 rms
+    oi = omoe.topk_select(ref_l, k)
+    bad = np.where((gi != oi).any(1))[0]
+    for t in bad:
+        srt = np.sort(ref_l[t])[::-1]
+        assert k < E and srt[k - 1] - srt[k] < 1e-4 * rms
+
+
+def test_route_all_equal_logits_picks_lowest_indices():
+    from split_weight_expert_amd import api
+    T, H, E, k = 70, 128, 100, 6
+    x = torch.randn(T, H, device=DEV).to(torch.bfloat16)
+    wr = torch.zeros(E, H, device=DEV, dtype=torch.bfloat16)
+    logits = torch.empty(T, E, device=DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, device=DEV)
+    api.route_topk(x, wr, None, k, logits, idx, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), np.tile(np.arange(k), (T, 1)))
+    np.testing.assert_array_equal(w.cpu().numpy(), np.full((T, k), np.float32(1.0 / k)))
+
+
+# --------------------------------------------------------------------------------------- permute
+
+def run_permute(idx_np, E, shared, x_t, act_dtype):
+    from split_weight_expert_amd import api
+    T, k = idx_np.shape
+    H = x_t.shape[1]
+    rows = T * k + shared * T
+    fp8 = act_dtype == api.FP8_E4M3
+    xp = torch.empty(rows, H, dtype=torch.uint8 if fp8 else x_t.dtype, device=DEV)
+    xs = torch.empty(rows, H // 128, dtype=torch.float32, device=DEV) if fp8 else None
+    off = torch.empty(E + shared + 1, dtype=torch.int32, device=DEV)
+    ps = torch.empty(rows, dtype=torch.int32, device=DEV)
+    ip = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    ws = torch.empty(api.workspace_bytes(api.OP_PERMUTE, T, k, E, H, 1, 1, shared), dtype=torch.uint8, device=DEV)
+    api.permute(torch.from_numpy(idx_np.astype(np.int32)).to(DEV), E, shared, x_t, act_dtype, xp, xs, off, ps, ip, ws)
+    torch.cuda.synchronize()
+    return xp, xs, off.cpu().numpy(), ps.cpu().numpy(), ip.cpu().numpy()
+
+
+PERM_CASES = [(64, 8, 2, 0), (1, 1, 1, 1), (1000, 256, 8, 1), (333, 17, 3, 1), (4097, 64, 4, 0), (2, 8, 8, 1)]
+
+
+@pytest.mark.parametrize("T,E,k,shared", PERM_CASES)
+def test_permute_parity_bf16(T, E, k, shared):
+    from split_weight_expert_amd import api
+    rng = np.random.default_rng(T * 7 + E)
+    idx = omoe.topk_select(rng.normal(size=(T, E)), k)
+    H = 256
+    x = torch.randn(T, H, device=DEV).to(torch.bfloat16)
+    xp, _, off, ps, ip = run_permute(idx, E, shared, x, api.BF16)
+    r_off, r_ps, r_ip, _ = omoe.permute(idx, E, shared)
+    np.testing.assert_array_equal(off, r_off)
+    np.testing.assert_array_equal(ps, r_ps)
+    np.testing.assert_array_equal(ip, r_ip)
+    xb = x.view(torch.int16).cpu().numpy()
+    np.testing.assert_array_equal(xp.view(torch.int16).cpu().numpy(), xb[r_ps])
+
+
+def test_permute_skewed_and_empty_experts():
+    from split_weight_expert_amd import api
+    T, E, k = 3000, 32, 2
+    idx = np.zeros((T, k), np.int32)
+    idx[:, 0] = 5
+    idx[:, 1] = np.where(np.arange(T) % 3 == 0, 9, 31)
+    x = torch.randn(T, 128, device=DEV)
+    xp, _, off, ps, ip = run_permute(idx, E, 1, x, api.F32)
+    r_off, r_ps, r_ip, _ = omoe.permute(idx, E, 1)
+    np.testing.assert_array_equal(off, r_off)
+    np.testing.assert_array_equal(ps, r_ps)
+    np.testing.assert_array_equal(ip, r_ip)
+    np.testing.assert_array_equal(xp.cpu().numpy(), x.cpu().numpy()[r_ps])
+
+
+@pytest.mark.parametrize("T", [1, 64, 515])
+def test_permute_fp8_quantisation_is_bit_exact(T):
+    from split_weight_expert_amd import api
+    rng = np.random.default_rng(T)
+    E, k, H = 16, 4, 512
+    idx = omoe.topk_select(rng.normal(size=(T, E)), k)
+    xf = rng.normal(0, 1, size=(T, H)).astype(np.float32)
+    xf[0, :128] = 0.0                                      # an all-zero group
+    if T > 3:
+        xf[3, 200] = 3000.0                                # a dominant element
+    x = torch.from_numpy(xf).to(DEV).to(torch.bfloat16)
+    xq, xs, off, ps, ip = run_permute(idx, E, 1, x, api.FP8_E4M3)
+    xv = x.float().cpu().numpy()
+    q_ref, s_ref = omoe.quantize_groups(xv)
+    r_off, r_ps, _, _ = omoe.permute(idx, E, 1)
+    np.testing.assert_array_equal(ps, r_ps)
+    np.testing.assert_array_equal(xq.cpu().numpy(), q_ref[r_ps])
+    np.testing.assert_array_equal(xs.cpu().numpy(), s_ref[r_ps])
+
+
+def test_e4m3_device_encoder_on_every_bf16_pattern():
+    """The device encoder (through per-token quantisation with unit scales) on all 65536 bf16 inputs."""
+    from split_weight_expert_amd import api
+    bits = np.arange(2 ** 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448.0)]
+    # every row holds 448 at column 0 so that its scale is exactly 1
+    n = -(-len(vals) // 127)
+    rows = np.zeros((n, 128), np.float32)
+    rows[:, 0] = 448.0
+    flat = np.zeros(n * 127, np.float32)
+    flat[:len(vals)] = vals
+    rows[:, 1:] = flat.reshape(n, 127)
+    x = torch.from_numpy(rows).to(DEV).to(torch.bfloat16)
+    idx = np.zeros((n, 1), np.int32)
+    xq, xs, *_ = run_permute(idx, 1, 0, x, api.FP8_E4M3)
+    assert np.all(xs.cpu().numpy() == 1.0)
+    np.testing.assert_array_equal(xq.cpu().numpy(), codecs.e4m3_encode(rows))
+
+
+# --------------------------------------------------------------------------------------- weights fp8
+
+def test_weight_block_quantisation_is_bit_exact():
+    from split_weight_expert_amd import api
+    rng = np.random.default_rng(3)
+    w = rng.normal(0, 0.02, size=(384, 640)).astype(np.float32)
+    w[0:128, 128:256] = 0.0
+    w[200, 300] = 5.0
+    wt = torch.from_numpy(w).to(DEV)
+    q = torch.empty(384, 640, dtype=torch.uint8, device=DEV)
+    s = torch.empty(3, 5, dtype=torch.float32, device=DEV)
+    api.quantize_weight_fp8(wt, q, s)
+    torch.cuda.synchronize()
+    qr, sr = omoe.quantize_blocks(w)
+    np.testing.assert_array_equal(q.cpu().numpy(), qr)
+    np.testing.assert_array_equal(s.cpu().numpy(), sr)
+
+
+# --------------------------------------------------------------------------------------- grouped FFN
+
+FFN_CASES = {
+    "f32": ("tiny_f32", dict(T=200)),
+    "bf16": ("prefill8k_bf16", dict(T=200, H=512, I=256, E=8, k=2, n_local=4)),
+    "fp8": ("prefill16k_fp8", dict(T=200, H=512, I=256, E=8, k=2, n_local=4)),
+}
+
+
+def skew_bias(E):
+    b = np.zeros(E, np.float32)
+    b[0] = 6.0          # most tokens pick expert 0: several m-tiles
+    b[E - 1] = -60.0    # nobody picks the last expert: an empty group
+    return b
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "fp8"])
+def test_grouped_ffn_parity(dt):
+    from split_weight_expert_amd import MoEBlock
+    name, kw = FFN_CASES[dt]
+    cfg = shrink(synth.get_config(name), **kw)
+    h = HostLayer(cfg, bias=skew_bias(cfg.E))
+    pl, slots = placement_split(cfg)
+    store, table, x, wr, b = upload_layer(h, pl, slots)
+    blk = MoEBlock(cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, cfg.dtype, DEV)
+    bb = blk.buffers(cfg.T)
+    blk.route(x, wr, b, bb)
+    blk.permute(x, bb)
+    blk.ffn(table, bb)
+    torch.cuda.synchronize()
+    off = bb.offsets.cpu().numpy()
+    ps = bb.perm_src.cpu().numpy()
+    counts = np.diff(off)
+    assert counts[0] > 128 and counts[cfg.E - 1] == 0
+    y_perm = to_np(bb.y_perm).astype(np.float64)
+    ws = list(h.experts) + ([h.shared] if h.shared is not None else [])
+    ref = np.zeros_like(y_perm)
+    X = omoe.prepare_tokens(h.x[ps], cfg.dtype)     # fp8: the oracle's own per-token quantisation
+    for g in range(len(ws)):
+        r0, r1 = off[g], off[g + 1]
+        if r1 > r0:
+            wg, wu, wd = omoe.prepare_weights(*ws[g], cfg.dtype)
+            ref[r0:r1] = omoe.expert_ffn(X[r0:r1], wg, wu, wd, cfg.dtype)
+    assert_close(y_perm, ref, dt, f"grouped ffn {dt}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "fp8"])
+def test_block_parity(dt):
+    from split_weight_expert_amd import MoEBlock
+    name, kw = FFN_CASES[dt]
+    cfg = shrink(synth.get_config(name), **kw)
+    h = HostLayer(cfg)
+    pl, slots = placement_split(cfg)
+    store, table, x, wr, b = upload_layer(h, pl, slots)
+    blk = MoEBlock(cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, cfg.dtype, DEV)
+    bb = blk.forward(x, wr, b, table)
+    torch.cuda.synchronize()
+    gl = bb.logits.cpu().numpy().astype(np.float64)
+    gi = bb.idx.cpu().numpy()
+    np.testing.assert_array_equal(gi, omoe.topk_select(gl, cfg.k))
+    # the oracle's layer on the GPU's routing decisions (the routing itself is checked bit-exactly)
+    ref = h.oracle(routing=(gl, gi, omoe.gate_weights(gl, gi)))
+    np.testing.assert_array_equal(bb.offsets.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(bb.inv_perm.cpu().numpy(), ref["inv_perm"])
+    assert_close(to_np(bb.y), ref["y"], dt, f"block {dt}")
+    # the oracle's own routing agrees wherever its selection margin is not tiny
+    own = h.oracle()
+    same = (own["idx"] == gi).all(1)
+    assert same.mean() > 0.99
+    assert_close(to_np(bb.y)[same], own["y"][same], dt, f"block {dt} (oracle routing)")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_placement_invariance_and_determinism(dt):
+    from split_weight_expert_amd import MoEBlock
+    name, kw = FFN_CASES[dt]
+    cfg = shrink(synth.get_config(name), **kw)
+    h = HostLayer(cfg)
+    G = cfg.E + cfg.shared
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(G)
+    placements = {
+        "split": placement_split(cfg),
+        "all_local": ([(0, g) for g in range(G)], [G, 1]),
+        "all_prefetch": ([(1, g) for g in range(G)], [1, G]),
+        "scattered": ([(int(perm[g] % 3), int(perm[g] // 3)) for g in range(G)], [-(-G // 3)] * 3),
+    }
+    outs = {}
+    for nm, (pl, slots) in placements.items():
+        store, table, x, wr, b = upload_layer(h, pl, slots)
+        blk = MoEBlock(cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, cfg.dtype, DEV)
+        y1 = blk.forward(x, wr, b, table).y.clone()
+        y2 = blk.forward(x, wr, b, table).y.clone()
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), f"{nm}: not deterministic"
+        outs[nm] = y1
+        del store
+    ref = outs["split"].view(torch.int16)
+    for nm, y in outs.items():
+        assert torch.equal(y.view(torch.int16), ref), f"placement {nm} changed the output"
+
+
+def test_redundant_placement_two_groups_share_one_record():
+    """Two groups pointing at the same record behave like two copies of the same expert."""
+    from split_weight_expert_amd import MoEBlock
+    name, kw = FFN_CASES["bf16"]
+    cfg = shrink(synth.get_config(name), **kw)
+    h = HostLayer(cfg)
+    h.experts[3] = h.experts[2]
+    pl, slots = placement_split(cfg)
+    store, table, x, wr, b = upload_layer(h, pl, slots)
+    pl2 = list(pl)
+    pl2[3] = pl[2]                                          # group 3 reads group 2's record
+    table2 = store.table(pl2, DEV)
+    blk = MoEBlock(cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, cfg.dtype, DEV)
+    y1 = blk.forward(x, wr, b, table).y.clone()
+    y2 = blk.forward(x, wr, b, table2).y.clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# --------------------------------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("dt,shared", [("f32", 0), ("bf16", 1), ("bf16", 0)])
+def test_combine_parity(dt, shared):
+    from split_weight_expert_amd import api
+    rng = np.random.default_rng(5)
+    T, k, H = 300, 8, 1024
+    rows = T * k + shared * T
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    yp = torch.randn(rows, H, device=DEV).to(tdt)
+    inv = np.stack([rng.permutation(T * k)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    y = torch.empty(T, H, dtype=tdt, device=DEV)
+    api.combine(yp, torch.from_numpy(inv).to(DEV), torch.from_numpy(w).to(DEV), shared, y)
+    torch.cuda.synchronize()
+    ypn = to_np(yp)
+    ref = np.stack([omoe.combine(ypn[inv[t]], w[t], ypn[T * k + t] if shared else None, dt) for t in range(T)])
+    assert_close(to_np(y), ref, dt, "combine")
+
+
+# --------------------------------------------------------------------------------------- prefetch
+
+@pytest.mark.parametrize("engine", [0, 1])
+def test_prefetch_copies_every_byte(engine):
+    from split_weight_expert_amd import api
+    rng = np.random.default_rng(engine)
+    sizes = [1_000_000, 3_333_344, 0, 2_097_152]
+    chunk = 262_144
+    srcs_np = [rng.integers(0, 256, size=n, dtype=np.uint8) for n in sizes]
+    srcs = [torch.from_numpy(a).to(DEV) if len(a) else torch.empty(16, dtype=torch.uint8, device=DEV)
+            for a in srcs_np]
+    offs = [0, 1_000_000, 4_333_344, 4_333_344]
+    total = offs[-1] + sizes[-1] + 64
+    dst = torch.full((total,), 7, dtype=torch.uint8, device=DEV)
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    done = torch.cuda.Event()
+    api.prefetch_chunks(dst.data_ptr(), [(s.data_ptr(), o, n) for s, o, n in zip(srcs, offs, sizes)], chunk,
+                        engine=engine, max_workgroups=5, copy_stream=cs, done_event=done)
+    torch.cuda.current_stream().wait_event(done)
+    got = dst.cpu().numpy()
+    ref = apply_plan(np.full(total, 7, np.uint8), srcs_np, offs, chunk)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_prefetch_waits_for_the_last_reader():
+    """The copy must not start before the event it is told to wait on (the last reader of the slots)."""
+    from split_weight_expert_amd import api
+    n = 64 << 20
+    src = torch.full((n,), 3, dtype=torch.uint8, device=DEV)
+    dst = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    reader = torch.cuda.Stream()
+    cs = torch.cuda.Stream()
+    snap = torch.empty(n, dtype=torch.uint8, device=DEV)
+    gate = torch.cuda.Event()
+    done = torch.cuda.Event()
+    reader.wait_stream(torch.cuda.current_stream())
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(reader):
+        torch.cuda._sleep(50_000_000)                       # keep the reader busy for a while
+        snap.copy_(dst)                                     # the reader's view of the slots
+        gate.record(reader)
+    api.prefetch_chunks(dst.data_ptr(), [(src.data_ptr(), 0, n)], 4 << 20, engine=1, copy_stream=cs,
+                        wait_event=gate, done_event=done)
+    torch.cuda.synchronize()
+    assert int(snap.max()) == 0                             # the reader saw the old contents
+    assert int(dst.min()) == 3                              # and the copy then completed
