@@ -114,7 +114,8 @@ typedef struct {
  * this softmax top-k gate with renormalisation over the chosen k is the
  * reading taken.
  *   x [T,H], w_router [E,H]: DWDP_F32 or DWDP_BF16 (in_dtype), 16-byte aligned.
- *   bias [E] fp32 or NULL.   1 <= k <= E <= 1024, k <= 32, H % 8 == 0.
+ *   bias [E] fp32 or NULL.   1 <= k <= E <= 1024, k <= 32; H % 64 == 0 (bf16) or
+ *   H % 16 == 0 (f32).
  *   logits_out [T,E] fp32, topk_idx [T,k] int32, topk_w [T,k] fp32. */
 int dwdp_route_topk(const void* x, const void* w_router, int in_dtype, const float* bias,
                     int64_t T, int H, int E, int k,
@@ -154,6 +155,15 @@ int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, int shared,
 int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,
                          const void* x_perm, const float* x_perm_scale, int64_t rows, int H, int I,
                          int w_dtype, void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* The grouped FFN in two halves, for callers that enqueue or time them apart:
+ * stage 1 builds the tile schedule and runs GEMM1 + SwiGLU, leaving A in ws;
+ * stage 2 runs GEMM2 from the A left in ws by a stage-1 call with the same
+ * arguments (and nothing else writing ws in between); stage 0 runs both and is
+ * dwdp_moe_grouped_ffn.  y_perm may be NULL for stage 1. */
+int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,
+                               const void* x_perm, const float* x_perm_scale, int64_t rows, int H, int I,
+                               int w_dtype, void* y_perm, void* ws, size_t ws_bytes, void* stream);
 
 /* Combine: y[t] = sum_{j<k} topk_w[t,j] * y_perm[inv_perm[t,j]] (+ y_perm[T*k + t]
  * when shared), summed in fp32 in slot order then the shared row, rounded once

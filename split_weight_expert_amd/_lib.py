@@ -43,6 +43,8 @@ SIGNATURES = {
     "dwdp_permute": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                             _vp]),
     "dwdp_moe_grouped_ffn": (_i32, [_vp, _i32, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "dwdp_moe_grouped_ffn_stage": (_i32, [_i32, _vp, _i32, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _sz,
+                                          _vp]),
     "dwdp_combine": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
     "dwdp_prefetch_chunks": (_i32, [_vp, _vp, _i32, _sz, _i32, _i32, _vp, _vp, _vp]),
     "dwdp_prefetch_plan": (_i32, [_vp, _i32, _sz, _vp, _sz, ctypes.POINTER(_sz)]),
@@ -63,6 +65,10 @@ def load(path: str = LIB_PATH):
     """Load libdwdp.so and attach the C signatures; raises if it is not built."""
     global _lib
     if _lib is None:
+        # torch ships its own HIP runtime (same soname, libamdhip64.so.7).  Loading it first makes this
+        # library bind to that same runtime instance; a second HIP runtime in the process cannot open
+        # the GPU once torch's has.
+        import torch  # noqa: F401
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built (run __graft_entry__.build()); there is no fallback path")
         lib = ctypes.CDLL(path)

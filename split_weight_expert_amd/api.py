@@ -25,9 +25,12 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _event(ev):
+def _event(ev, stream=None):
+    """hipEvent_t of a torch event; torch creates events lazily, so an unrecorded one is first recorded."""
     if ev is None:
         return None
+    if ev.cuda_event == 0:
+        ev.record(torch.cuda.current_stream() if stream is None else stream)
     return ctypes.c_void_p(ev.cuda_event)
 
 
@@ -68,6 +71,15 @@ def moe_grouped_ffn(table, n_groups, offsets, x_perm, x_perm_scale, H, I, w_dtyp
                                                 _stream(stream)))
 
 
+def moe_grouped_ffn_stage(stage, table, n_groups, offsets, x_perm, x_perm_scale, H, I, w_dtype, y_perm, ws,
+                          stream=None):
+    rows = x_perm.shape[0]
+    _lib.check(_lib.load().dwdp_moe_grouped_ffn_stage(stage, _ptr(table), n_groups, _ptr(offsets), _ptr(x_perm),
+                                                      _ptr(x_perm_scale), rows, H, I, w_dtype, _ptr(y_perm),
+                                                      _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                                      _stream(stream)))
+
+
 def combine(y_perm, inv_perm, topk_w, shared, y, stream=None):
     T, k = inv_perm.shape
     H = y.shape[1]
@@ -90,7 +102,7 @@ def prefetch_chunks(dst_ptr, srcs, chunk_bytes, engine=COPY_KERNEL, max_workgrou
     arr = _sources(srcs)
     _lib.check(_lib.load().dwdp_prefetch_chunks(ctypes.c_void_p(dst_ptr), arr, len(srcs), chunk_bytes, engine,
                                                 max_workgroups, _stream(copy_stream), _event(wait_event),
-                                                _event(done_event)))
+                                                _event(done_event, copy_stream)))
 
 
 def prefetch_plan(srcs, chunk_bytes):

@@ -552,14 +552,19 @@ void launch_schedule(const int32_t* offsets, int G, int32_t* pre, MTile* mt, hip
     hipLaunchKernelGGL(schedule_kernel<BM>, dim3(1), dim3(1024), 0, st, offsets, G, pre, mt);
 }
 
+// decode_tile gives XCD x the slots x, x+8, x+16, ... of a stretch of ceil(total/8) tiles, so the
+// launch must hold whole rounds of 8 workgroups: round the tile bound up to a multiple of 8.
+int64_t xcd_grid(int64_t tiles) { return (tiles + kNumXcd - 1) / kNumXcd * kNumXcd; }
+
 template <int BM, int BN, int WM, int WN, int KIND, bool FP8>
-void launch_mfma(const GemmParams& p, int64_t grid, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, KIND, FP8>), dim3((unsigned)grid), dim3(WM * WN * 64), 0, st, p);
+void launch_mfma(const GemmParams& p, int64_t tiles, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, KIND, FP8>), dim3((unsigned)xcd_grid(tiles)),
+                       dim3(WM * WN * 64), 0, st, p);
 }
 
 template <int KIND>
-void launch_f32(const GemmParams& p, int64_t grid, hipStream_t st) {
-    hipLaunchKernelGGL(gemm_f32_kernel<KIND>, dim3((unsigned)grid), dim3(256), 0, st, p);
+void launch_f32(const GemmParams& p, int64_t tiles, hipStream_t st) {
+    hipLaunchKernelGGL(gemm_f32_kernel<KIND>, dim3((unsigned)xcd_grid(tiles)), dim3(256), 0, st, p);
 }
 
 }  // namespace
@@ -599,10 +604,12 @@ int router_gemm(const void* x, const void* w, int dtype, const float* bias, int6
 
 using namespace dwdp;
 
-extern "C" int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,
-                                    const void* x_perm, const float* x_perm_scale, int64_t rows, int H, int I,
-                                    int w_dtype, void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* table, int n_groups,
+                                          const int32_t* offsets, const void* x_perm, const float* x_perm_scale,
+                                          int64_t rows, int H, int I, int w_dtype, void* y_perm, void* ws,
+                                          size_t ws_bytes, void* stream) {
     clear_error();
+    DWDP_REQUIRE(stage >= 0 && stage <= 2, "stage must be 0, 1 or 2");
     DWDP_REQUIRE(w_dtype == DWDP_F32 || w_dtype == DWDP_BF16 || w_dtype == DWDP_FP8_E4M3, "unknown w_dtype");
     DWDP_REQUIRE(n_groups >= 1 && n_groups <= (1 << 20), "n_groups out of range");
     DWDP_REQUIRE(rows >= 0 && rows < (int64_t)1 << 31, "rows out of range");
@@ -613,7 +620,7 @@ extern "C" int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups,
         DWDP_REQUIRE(H % 128 == 0 && I % 128 == 0, "bf16/fp8 paths need H % 128 == 0 and I % 128 == 0");
     }
     if (rows == 0) return DWDP_OK;
-    DWDP_REQUIRE(table && offsets && x_perm && y_perm && ws, "null pointer argument");
+    DWDP_REQUIRE(table && offsets && x_perm && ws && (y_perm || stage == 1), "null pointer argument");
     DWDP_REQUIRE(aligned16(table) && aligned16(x_perm) && aligned16(y_perm) && aligned16(ws),
                  "pointers must be 16-byte aligned");
     if (w_dtype == DWDP_FP8_E4M3) DWDP_REQUIRE(x_perm_scale != nullptr, "fp8 needs x_perm_scale");
@@ -667,20 +674,28 @@ extern "C" int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups,
     const int64_t grid1 = L.maxm1 * p1.NT, grid2 = (s.bm1 == s.bm2 ? L.maxm1 : L.maxm2) * p2.NT;
     DWDP_REQUIRE(grid1 < ((int64_t)1 << 31) && grid2 < ((int64_t)1 << 31), "problem too large for one launch");
 
+    const bool g1 = stage != 2, g2 = stage != 1;
     if (w_dtype == DWDP_BF16) {
-        launch_schedule<kBmBf16>(offsets, n_groups, pre1, mt1, st);
-        launch_mfma<kBmBf16, kBnBf16, 2, 2, kGemm1, false>(p1, grid1, st);
-        launch_mfma<kBmBf16, kBnBf16, 2, 2, kGemm2, false>(p2, grid2, st);
+        if (g1) launch_schedule<kBmBf16>(offsets, n_groups, pre1, mt1, st);
+        if (g1) launch_mfma<kBmBf16, kBnBf16, 2, 2, kGemm1, false>(p1, grid1, st);
+        if (g2) launch_mfma<kBmBf16, kBnBf16, 2, 2, kGemm2, false>(p2, grid2, st);
     } else if (w_dtype == DWDP_FP8_E4M3) {
-        launch_schedule<kBmFp8G1>(offsets, n_groups, pre1, mt1, st);
-        launch_schedule<kBmFp8G2>(offsets, n_groups, pre2, mt2, st);
-        launch_mfma<kBmFp8G1, kBnFp8G1, 1, 4, kGemm1, true>(p1, grid1, st);
-        launch_mfma<kBmFp8G2, kBnFp8G2, 2, 2, kGemm2, true>(p2, grid2, st);
+        if (g1) launch_schedule<kBmFp8G1>(offsets, n_groups, pre1, mt1, st);
+        if (g1) launch_schedule<kBmFp8G2>(offsets, n_groups, pre2, mt2, st);
+        if (g1) launch_mfma<kBmFp8G1, kBnFp8G1, 1, 4, kGemm1, true>(p1, grid1, st);
+        if (g2) launch_mfma<kBmFp8G2, kBnFp8G2, 2, 2, kGemm2, true>(p2, grid2, st);
     } else {
-        launch_schedule<kBmF32>(offsets, n_groups, pre1, mt1, st);
-        launch_f32<kGemm1>(p1, grid1, st);
-        launch_f32<kGemm2>(p2, grid2, st);
+        if (g1) launch_schedule<kBmF32>(offsets, n_groups, pre1, mt1, st);
+        if (g1) launch_f32<kGemm1>(p1, grid1, st);
+        if (g2) launch_f32<kGemm2>(p2, grid2, st);
     }
     DWDP_LAUNCHED();
     return DWDP_OK;
+}
+
+extern "C" int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,
+                                    const void* x_perm, const float* x_perm_scale, int64_t rows, int H, int I,
+                                    int w_dtype, void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+    return dwdp_moe_grouped_ffn_stage(0, table, n_groups, offsets, x_perm, x_perm_scale, rows, H, I, w_dtype, y_perm,
+                                      ws, ws_bytes, stream);
 }

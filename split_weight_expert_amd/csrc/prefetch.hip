@@ -149,16 +149,11 @@ extern "C" int dwdp_prefetch_chunks(void* dst, const dwdp_copy_src* srcs, int n_
     hipStream_t st = as_stream(copy_stream);
     std::vector<dwdp_chunk> plan = make_plan(srcs, n_src, chunk_bytes);
     if (!plan.empty()) DWDP_REQUIRE(dst != nullptr, "dst is NULL");
-    if (wait_event) DWDP_HIP(hipStreamWaitEvent(st, reinterpret_cast<hipEvent_t>(wait_event), 0));
-    if (engine == DWDP_COPY_HIPMEMCPY) {
-        for (const dwdp_chunk& c : plan) {
-            DWDP_HIP(hipMemcpyAsync(static_cast<uint8_t*>(dst) + c.dst_offset,
-                                    static_cast<const uint8_t*>(srcs[c.source].src) + c.src_offset, c.bytes,
-                                    hipMemcpyDeviceToDevice, st));
-        }
-    } else if (!plan.empty()) {
+    CopyArgs a{};
+    if (engine == DWDP_COPY_KERNEL && !plan.empty()) {
+        // validate everything before anything is enqueued
         DWDP_REQUIRE(chunk_bytes % 16 == 0, "kernel engine needs chunk_bytes % 16 == 0");
-        CopyArgs a{};
+        DWDP_REQUIRE(aligned16(dst), "kernel engine needs a 16-byte aligned dst");
         a.dst = static_cast<uint8_t*>(dst);
         a.chunk = chunk_bytes;
         a.n_src = n_src;
@@ -175,8 +170,16 @@ extern "C" int dwdp_prefetch_chunks(void* dst, const dwdp_copy_src* srcs, int n_
             a.nchunks[s] = (int32_t)nc;
             rounds = std::max(rounds, nc);
         }
-        DWDP_REQUIRE(aligned16(dst), "kernel engine needs a 16-byte aligned dst");
         a.max_rounds = (int32_t)rounds;
+    }
+    if (wait_event) DWDP_HIP(hipStreamWaitEvent(st, reinterpret_cast<hipEvent_t>(wait_event), 0));
+    if (engine == DWDP_COPY_HIPMEMCPY) {
+        for (const dwdp_chunk& c : plan) {
+            DWDP_HIP(hipMemcpyAsync(static_cast<uint8_t*>(dst) + c.dst_offset,
+                                    static_cast<const uint8_t*>(srcs[c.source].src) + c.src_offset, c.bytes,
+                                    hipMemcpyDeviceToDevice, st));
+        }
+    } else if (!plan.empty()) {
         const int grid = (int)std::min<int64_t>(max_workgroups > 0 ? max_workgroups : 32, a.total_chunks);
         hipLaunchKernelGGL(slice_copy_kernel, dim3(grid), dim3(256), 0, st, a);
         DWDP_LAUNCHED();

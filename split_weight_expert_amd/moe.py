@@ -150,6 +150,10 @@ class MoEBlock:
         api.moe_grouped_ffn(table, self.E + self.shared, b.offsets, b.x_perm, b.x_perm_scale, self.H, self.I,
                             self.w_dtype, b.y_perm, b.ws_ffn, stream)
 
+    def ffn_stage(self, stage: int, table, b: BlockBuffers, stream=None):
+        api.moe_grouped_ffn_stage(stage, table, self.E + self.shared, b.offsets, b.x_perm, b.x_perm_scale, self.H,
+                                  self.I, self.w_dtype, b.y_perm, b.ws_ffn, stream)
+
     def combine(self, b: BlockBuffers, stream=None):
         api.combine(b.y_perm, b.inv_perm, b.w, self.shared, b.y, stream)
 

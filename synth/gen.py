@@ -77,6 +77,7 @@ def _host_lib():
 def _gpu_lib():
     global _gpu
     if _gpu is None:
+        import torch  # noqa: F401  -- bind to torch's HIP runtime instance (see split_weight_expert_amd._lib)
         if not os.path.exists(GPU_LIB):
             raise RuntimeError(f"{GPU_LIB} is not built; run __graft_entry__.build()")
         lib = ctypes.CDLL(GPU_LIB)
