@@ -43,7 +43,31 @@ def parse():
     ap.add_argument("--no-prefetch", action="store_true", help="skip the prefetch / overlap measurement")
     ap.add_argument("--copy-workgroups", type=int, default=32)
     ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy"])
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run the slice-copy kernel on BYTES bytes (HBM counter calibration) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(nbytes, reps=3):
+    """A plain copy of known size through the library's slice-copy kernel (one source, 4 MiB slices)."""
+    import torch
+
+    from split_weight_expert_amd import api
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        api.prefetch_chunks(dst.data_ptr(), [(src.data_ptr(), 0, nbytes)], 4 << 20, engine=api.COPY_KERNEL,
+                            max_workgroups=256, copy_stream=torch.cuda.current_stream())
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1))
+    ok = bool(torch.equal(src[-4096:], dst[-4096:]))
+    print(json.dumps(dict(calibrate_copy_bytes=nbytes, ms=float(np.median(t)),
+                          gbps=nbytes / float(np.median(t)) / 1e6, ok=ok)), flush=True)
 
 
 def log(msg):
@@ -99,10 +123,13 @@ def main():
               "described in DESIGN.md but not built", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
     import torch
 
     import synth
-    from split_weight_expert_amd import api
     from split_weight_expert_amd.workload import DeviceLayer
 
     cfg = synth.get_config(args.workload)

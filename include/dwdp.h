@@ -148,7 +148,7 @@ int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, int shared,
  *     codes + 128x128 block scales; products accumulated in fp32 per 128-wide K
  *     block and scaled by (row scale * block scale); A quantised per row and
  *     128-column group like x; y_perm bf16.
- *   rows must equal offsets[n_groups] (not checked on the device).  H % 128 == 0,
+ *   rows must equal offsets[n_groups] (not checked on the device).  H % 256 == 0,
  *   I % 128 == 0 (BF16/FP8); H % 4, I % 4 == 0 (F32).  offsets is read on the
  *   device only; no host synchronisation happens.
  *   ws: dwdp_workspace_bytes(DWDP_OP_GROUPED_FFN, ...) bytes (holds A). */

@@ -425,6 +425,250 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(GemmParams p) {
     }
 }
 
+// ------------------------------------------------------------------------------ LDS-DMA kernel
+// The expert GEMMs.  One workgroup of 4 waves per CU computes a BM x 256 tile; the waves split the
+// 256 weight rows (64 each) and share all BM activation rows, so a short tail tile skips whole
+// 32-row m-blocks in every wave.  Operand slices of 128 bytes per row go straight from global
+// memory into a 3-stage LDS ring (global_load_lds_dwordx4: no register staging), two K steps
+// ahead of the MFMAs; each wave waits only for its own oldest stage (vmcnt) and one barrier per
+// step orders the ring.  XOR-swizzled 16-byte chunks keep the ds_read_b128 fragment reads
+// conflict-free.
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at lds + 16 * l
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void ordered_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BM, int KIND, bool FP8>
+__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
+    constexpr int BN = 256, NW = 4, S = 3, ROWB = 128;
+    constexpr int MI = BM / 32, NJ = 2;
+    constexpr int AI = BM / 8 / NW, BI = BN / 8 / NW, PER = AI + BI;
+    constexpr int STAGE = (BM + BN) * ROWB;
+    static_assert(AI >= 1 && BM % 32 == 0, "BM must be 32, 64 or 128");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+
+    Tile t;
+    if (!decode_tile<BM, KIND>(p, t)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    const uint8_t* wbase;
+    const float* wscale;
+    if (KIND == kGemm1) {
+        wbase = static_cast<const uint8_t*>(p.table[t.g].w13);
+        wscale = p.table[t.g].s13;
+    } else {
+        wbase = static_cast<const uint8_t*>(p.table[t.g].w2);
+        wscale = p.table[t.g].s2;
+    }
+    const size_t ldk = (size_t)p.K * (FP8 ? 1 : 2);
+    const int KT = p.K / (FP8 ? 128 : 64);
+
+    auto w_row = [&](int r) -> int {
+        if (KIND == kGemm1) return r < BN / 2 ? t.nt * (BN / 2) + r : p.I + t.nt * (BN / 2) + (r - BN / 2);
+        return t.nt * BN + r;
+    };
+    // tile row of the first row of this wave's n-block j (GEMM1: j = 0 gate, j = 1 up)
+    auto b_block_row = [&](int j) -> int { return KIND == kGemm1 ? j * (BN / 2) + wave * 32 : wave * 64 + j * 32; };
+    auto row_of = [&](int i, int r) -> int { return i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3); };
+
+    // lane l of a load instruction fills LDS row (l/8) position (l%8) of an 8-row group; it fetches the
+    // logical chunk that the swizzle puts there
+    const uint8_t* ga[AI];
+    const uint8_t* gb[BI];
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+        const int r = (wave * AI + i) * 8 + (lane >> 3), c = (lane & 7) ^ (r & 7);
+        ga[i] = p.a + (size_t)(t.row0 + min(r, t.nrows - 1)) * ldk + c * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+        const int r = (wave * BI + i) * 8 + (lane >> 3), c = (lane & 7) ^ (r & 7);
+        gb[i] = wbase + (size_t)w_row(r) * ldk + c * 16;
+    }
+    auto issue = [&](int kt) {
+        uint8_t* st = smem + (kt % S) * STAGE;
+        const size_t off = (size_t)kt * ROWB;
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+            dma16(ga[i] + off, st + (wave * AI + i) * 8 * ROWB);
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+            dma16(gb[i] + off, st + BM * ROWB + (wave * BI + i) * 8 * ROWB);
+    };
+    auto lds16 = [&](const uint8_t* base, int row, int chunk) -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(base + row * ROWB + ((chunk ^ (row & 7)) << 4));
+    };
+
+    bool m_act[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) m_act[i] = i * 32 < t.nrows;
+
+    f32x16 acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    issue(0);
+    if (KT > 1) issue(1);
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) wait_vmcnt<PER>();
+        else wait_vmcnt<0>();
+        ordered_barrier();
+        // fp8 scales of this K block, loaded before the next DMA batch so that waiting for them does
+        // not wait for that batch too (vector memory loads complete in order)
+        [[maybe_unused]] float sb[NJ], sa[FP8 ? MI : 1][16];
+        if constexpr (FP8) {
+            const int KB = p.K / kFp8Group;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) sb[j] = wscale[(size_t)(w_row(b_block_row(j)) / kFp8Group) * KB + kt];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sa[i][r] = m_act[i] ? p.a_scale[(size_t)(t.row0 + min(row_of(i, r), t.nrows - 1)) * KB + kt] : 0.0f;
+        }
+        if (kt + 2 < KT) issue(kt + 2);
+        const uint8_t* A = smem + (kt % S) * STAGE;
+        const uint8_t* B = A + BM * ROWB;
+        if constexpr (!FP8) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int ch = s * 2 + hi;
+                bf16x8 af[MI], bf[NJ];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) bf[j] = __builtin_bit_cast(bf16x8, lds16(B, b_block_row(j) + l32, ch));
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    if (m_act[i]) af[i] = __builtin_bit_cast(bf16x8, lds16(A, i * 32 + l32, ch));
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    if (!m_act[i]) continue;
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                }
+            }
+        } else {
+            f32x16 part[MI][NJ];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int ch = s * 4 + hi * 2;
+                i32x8 af[MI], bf[NJ];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int row = b_block_row(j) + l32;
+                    const u32x4 lo = lds16(B, row, ch), up = lds16(B, row, ch + 1);
+                    bf[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2],
+                                  (int)up[3]};
+                }
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    if (!m_act[i]) continue;
+                    const u32x4 lo = lds16(A, i * 32 + l32, ch), up = lds16(A, i * 32 + l32, ch + 1);
+                    af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2],
+                                  (int)up[3]};
+                }
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    if (!m_act[i]) continue;
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+                        part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], part[i][j], 0, 0, 0,
+                                                                                     127, 0, 127);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                if (!m_act[i]) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) acc[i][j][r] += part[i][j][r] * (sa[i][r] * sb[j]);
+            }
+        }
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    if constexpr (KIND == kGemm1) {
+        const int col = t.nt * (BN / 2) + wave * 32 + l32;     // A column of this lane
+        if constexpr (!FP8) {
+            uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = row_of(i, r);
+                    if (m < t.nrows) out[(size_t)(t.row0 + m) * p.N + col] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
+                }
+        } else {
+            // the tile's 128 A columns are exactly one quantisation group: amax over the 4 waves
+            ordered_barrier();                                   // the ring is free: reuse it for the reduction
+            float* red = reinterpret_cast<float*>(smem);         // [NW][BM]
+            float av[MI][16];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    av[i][r] = silu_mul(acc[i][0][r], acc[i][1][r]);
+                    float m = fabsf(av[i][r]);
+#pragma unroll
+                    for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+                    if (l32 == 0) red[wave * BM + row_of(i, r)] = m;
+                }
+            __syncthreads();
+            const int IB = p.N / kFp8Group;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = row_of(i, r);
+                    const float amax = fmaxf(fmaxf(red[m], red[BM + m]), fmaxf(red[2 * BM + m], red[3 * BM + m]));
+                    const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+                    if (m < t.nrows) {
+                        p.out[(size_t)(t.row0 + m) * p.N + col] = f32_to_e4m3(av[i][r] / sc);
+                        if (wave == 0 && l32 == 0) p.out_scale[(size_t)(t.row0 + m) * IB + t.nt] = sc;
+                    }
+                }
+        }
+    } else {
+        uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = row_of(i, r);
+                    if (m < t.nrows)
+                        out[(size_t)(t.row0 + m) * p.N + t.nt * BN + wave * 64 + j * 32 + l32] = f32_to_bf16(acc[i][j][r]);
+                }
+    }
+}
+
 // ------------------------------------------------------------------------------ f32 kernel
 // 64 x 64 tile, 256 threads, 4 x 4 outputs per thread, K step 16.  Exact-ish
 // fp32 math (expf, IEEE division) for the small fp32 workload.
@@ -499,50 +743,42 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------------------------------------ configs
-// bf16: 128 x 128 tiles, 2 x 2 waves.  fp8 GEMM1: 64 x 256 (one 128-column A
-// group per tile), 1 x 4 waves; fp8 GEMM2: 128 x 128.  Router: 64 x 64.
-constexpr int kBmBf16 = 128, kBnBf16 = 128;
-constexpr int kBmFp8G1 = 64, kBnFp8G1 = 256;
-constexpr int kBmFp8G2 = 128, kBnFp8G2 = 128;
+// Expert GEMMs (bf16, fp8): gemm_dma_kernel, BM x 256 tiles with BM = 32, 64 or 128 picked from the
+// mean rows per group (decode batches give groups of a few rows).  f32: 64 x 64 FMA tiles.
+// Router (bf16): gemm_mfma_kernel, 64 x 64 tiles.
+constexpr int kBnDma = 256;
 constexpr int kBmF32 = 64, kBnF32 = 64;
 constexpr int kBmRouter = 64, kBnRouter = 64;
+constexpr int kBmMin = 32;
 
-struct FfnShape {
-    int bm1, bn1, bm2, bn2;
-};
-
-FfnShape ffn_shape(int dtype) {
-    if (dtype == DWDP_BF16) return {kBmBf16, kBnBf16, kBmBf16, kBnBf16};
-    if (dtype == DWDP_FP8_E4M3) return {kBmFp8G1, kBnFp8G1, kBmFp8G2, kBnFp8G2};
-    return {kBmF32, kBnF32, kBmF32, kBnF32};
+int choose_bm(int dtype, int64_t rows, int groups) {
+    if (dtype == DWDP_F32) return kBmF32;
+    const int64_t mean = rows / groups;
+    const int bm = mean >= 96 ? 128 : mean >= 40 ? 64 : 32;
+    return dtype == DWDP_FP8_E4M3 ? (bm > 64 ? 64 : bm) : bm;   // fp8 keeps a partial sum: 64 rows max
 }
 
 size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct FfnWs {
-    size_t a, a_scale, pre1, mt1, pre2, mt2, total;
-    int64_t maxm1, maxm2;
+    size_t a, a_scale, pre, mt, total;
 };
 
+// Workspace: A [rows, I] (+ fp8 scales), the m-tile prefix [G+1] and the m-tile table, sized for
+// the smallest BM so that any choice fits.
 FfnWs ffn_ws_layout(int64_t rows, int groups, int I, int dtype) {
-    FfnShape s = ffn_shape(dtype);
     FfnWs w{};
     const size_t ea = dtype == DWDP_F32 ? 4 : dtype == DWDP_BF16 ? 2 : 1;
-    w.maxm1 = (rows + s.bm1 - 1) / s.bm1 + groups;
-    w.maxm2 = (rows + s.bm2 - 1) / s.bm2 + groups;
+    const int64_t maxm = (rows + kBmMin - 1) / kBmMin + groups;
     size_t off = 0;
     w.a = off;
     off += a256((size_t)rows * I * ea);
     w.a_scale = off;
     if (dtype == DWDP_FP8_E4M3) off += a256((size_t)rows * (I / kFp8Group) * 4);
-    w.pre1 = off;
+    w.pre = off;
     off += a256((size_t)(groups + 1) * 4);
-    w.mt1 = off;
-    off += a256((size_t)w.maxm1 * sizeof(MTile));
-    w.pre2 = off;
-    off += a256((size_t)(groups + 1) * 4);
-    w.mt2 = off;
-    off += a256((size_t)w.maxm2 * sizeof(MTile));
+    w.mt = off;
+    off += a256((size_t)maxm * sizeof(MTile));
     w.total = off;
     return w;
 }
@@ -565,6 +801,28 @@ void launch_mfma(const GemmParams& p, int64_t tiles, hipStream_t st) {
 template <int KIND>
 void launch_f32(const GemmParams& p, int64_t tiles, hipStream_t st) {
     hipLaunchKernelGGL(gemm_f32_kernel<KIND>, dim3((unsigned)xcd_grid(tiles)), dim3(256), 0, st, p);
+}
+
+template <int BM, int KIND, bool FP8>
+void launch_dma(const GemmParams& p, int64_t tiles, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, KIND, FP8>), dim3((unsigned)xcd_grid(tiles)), dim3(256), 0, st, p);
+}
+
+template <int BM>
+void launch_ffn(bool g1, bool g2, bool fp8_path, const int32_t* offsets, int G, const GemmParams& p1,
+                const GemmParams& p2, int64_t maxm, hipStream_t st) {
+    if (g1) launch_schedule<BM>(offsets, G, const_cast<int32_t*>(p1.mprefix), const_cast<MTile*>(p1.mtiles), st);
+    if constexpr (BM <= 64) {
+        if (fp8_path) {
+            if (g1) launch_dma<BM, kGemm1, true>(p1, maxm * p1.NT, st);
+            if (g2) launch_dma<BM, kGemm2, true>(p2, maxm * p2.NT, st);
+            return;
+        }
+    }
+    {
+        if (g1) launch_dma<BM, kGemm1, false>(p1, maxm * p1.NT, st);
+        if (g2) launch_dma<BM, kGemm2, false>(p2, maxm * p2.NT, st);
+    }
 }
 
 }  // namespace
@@ -617,7 +875,7 @@ extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* tab
     if (w_dtype == DWDP_F32) {
         DWDP_REQUIRE(H % 64 == 0 && I % 32 == 0 && H % 16 == 0 && I % 16 == 0, "f32 path needs H % 64 == 0, I % 32 == 0");
     } else {
-        DWDP_REQUIRE(H % 128 == 0 && I % 128 == 0, "bf16/fp8 paths need H % 128 == 0 and I % 128 == 0");
+        DWDP_REQUIRE(H % 256 == 0 && I % 128 == 0, "bf16/fp8 paths need H % 256 == 0 and I % 128 == 0");
     }
     if (rows == 0) return DWDP_OK;
     DWDP_REQUIRE(table && offsets && x_perm && ws && (y_perm || stage == 1), "null pointer argument");
@@ -629,65 +887,45 @@ extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* tab
         return fail(DWDP_ERR_WORKSPACE, "dwdp_moe_grouped_ffn: workspace too small (need " + std::to_string(L.total) + ")");
     hipStream_t st = as_stream(stream);
     uint8_t* base = static_cast<uint8_t*>(ws);
-    uint8_t* A = base + L.a;
-    float* As = reinterpret_cast<float*>(base + L.a_scale);
-    int32_t* pre1 = reinterpret_cast<int32_t*>(base + L.pre1);
-    MTile* mt1 = reinterpret_cast<MTile*>(base + L.mt1);
-    int32_t* pre2 = reinterpret_cast<int32_t*>(base + L.pre2);
-    MTile* mt2 = reinterpret_cast<MTile*>(base + L.mt2);
-    FfnShape s = ffn_shape(w_dtype);
+    const int bm = choose_bm(w_dtype, rows, n_groups);
+    const int64_t maxm = (rows + bm - 1) / bm + n_groups;
 
     GemmParams p1{};
     p1.a = static_cast<const uint8_t*>(x_perm);
     p1.a_scale = x_perm_scale;
     p1.table = table;
     p1.offsets = offsets;
-    p1.mprefix = pre1;
-    p1.mtiles = mt1;
+    p1.mprefix = reinterpret_cast<int32_t*>(base + L.pre);
+    p1.mtiles = reinterpret_cast<MTile*>(base + L.mt);
     p1.G = n_groups;
     p1.N = I;
     p1.K = H;
     p1.I = I;
-    p1.NT = I / (s.bn1 / 2);
-    p1.out = A;
-    p1.out_scale = As;
+    p1.NT = w_dtype == DWDP_F32 ? I / (kBnF32 / 2) : I / (kBnDma / 2);
+    p1.out = base + L.a;
+    p1.out_scale = reinterpret_cast<float*>(base + L.a_scale);
 
-    GemmParams p2{};
-    p2.a = A;
-    p2.a_scale = As;
-    p2.table = table;
-    p2.offsets = offsets;
-    p2.G = n_groups;
+    GemmParams p2 = p1;
+    p2.a = base + L.a;
+    p2.a_scale = reinterpret_cast<const float*>(base + L.a_scale);
     p2.N = H;
     p2.K = I;
-    p2.I = I;
-    p2.NT = H / s.bn2;
+    p2.NT = w_dtype == DWDP_F32 ? H / kBnF32 : H / kBnDma;
     p2.out = static_cast<uint8_t*>(y_perm);
-
-    if (s.bm1 == s.bm2) {
-        p2.mprefix = pre1;
-        p2.mtiles = mt1;
-    } else {
-        p2.mprefix = pre2;
-        p2.mtiles = mt2;
-    }
-    const int64_t grid1 = L.maxm1 * p1.NT, grid2 = (s.bm1 == s.bm2 ? L.maxm1 : L.maxm2) * p2.NT;
-    DWDP_REQUIRE(grid1 < ((int64_t)1 << 31) && grid2 < ((int64_t)1 << 31), "problem too large for one launch");
+    p2.out_scale = nullptr;
+    DWDP_REQUIRE(maxm * p1.NT < ((int64_t)1 << 31) && maxm * p2.NT < ((int64_t)1 << 31),
+                 "problem too large for one launch");
 
     const bool g1 = stage != 2, g2 = stage != 1;
-    if (w_dtype == DWDP_BF16) {
-        if (g1) launch_schedule<kBmBf16>(offsets, n_groups, pre1, mt1, st);
-        if (g1) launch_mfma<kBmBf16, kBnBf16, 2, 2, kGemm1, false>(p1, grid1, st);
-        if (g2) launch_mfma<kBmBf16, kBnBf16, 2, 2, kGemm2, false>(p2, grid2, st);
-    } else if (w_dtype == DWDP_FP8_E4M3) {
-        if (g1) launch_schedule<kBmFp8G1>(offsets, n_groups, pre1, mt1, st);
-        if (g1) launch_schedule<kBmFp8G2>(offsets, n_groups, pre2, mt2, st);
-        if (g1) launch_mfma<kBmFp8G1, kBnFp8G1, 1, 4, kGemm1, true>(p1, grid1, st);
-        if (g2) launch_mfma<kBmFp8G2, kBnFp8G2, 2, 2, kGemm2, true>(p2, grid2, st);
+    if (w_dtype == DWDP_F32) {
+        if (g1) launch_schedule<kBmF32>(offsets, n_groups, const_cast<int32_t*>(p1.mprefix), const_cast<MTile*>(p1.mtiles), st);
+        if (g1) launch_f32<kGemm1>(p1, maxm * p1.NT, st);
+        if (g2) launch_f32<kGemm2>(p2, maxm * p2.NT, st);
     } else {
-        if (g1) launch_schedule<kBmF32>(offsets, n_groups, pre1, mt1, st);
-        if (g1) launch_f32<kGemm1>(p1, grid1, st);
-        if (g2) launch_f32<kGemm2>(p2, grid2, st);
+        const bool fp8 = w_dtype == DWDP_FP8_E4M3;
+        if (bm == 128 && !fp8) launch_ffn<128>(g1, g2, false, offsets, n_groups, p1, p2, maxm, st);
+        else if (bm == 64) launch_ffn<64>(g1, g2, fp8, offsets, n_groups, p1, p2, maxm, st);
+        else launch_ffn<32>(g1, g2, fp8, offsets, n_groups, p1, p2, maxm, st);
     }
     DWDP_LAUNCHED();
     return DWDP_OK;

@@ -83,7 +83,7 @@ def test_grouped_ffn_rejects_bad_arguments(lib):
     f = lib.dwdp_moe_grouped_ffn
     E_ = lib_mod.DWDP_ERR_INVALID_ARG
     expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7168, 2048, 5, FAKE, FAKE, 1 << 30, None), lib, "w_dtype")
-    expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7000, 2048, 1, FAKE, FAKE, 1 << 30, None), lib, "H % 128")
+    expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7040, 2048, 1, FAKE, FAKE, 1 << 30, None), lib, "H % 256")
     expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7168, 2048, 2, FAKE, FAKE, 1 << 30, None), lib, "x_perm_scale")
     expect(E_, f(FAKE, 9, FAKE, ODD, None, 128, 7168, 2048, 1, FAKE, FAKE, 1 << 30, None), lib, "aligned")
     expect(lib_mod.DWDP_ERR_WORKSPACE, f(FAKE, 9, FAKE, FAKE, None, 128, 7168, 2048, 1, FAKE, FAKE, 64, None),
