@@ -38,6 +38,7 @@
  *   w_router   [E, H]            router weight, same dtype as x
  *   expert e   W13 [2I, H]       gate rows 0..I-1, then up rows (Wg stacked on Wu)
  *              W2  [H, I]        down projection
+ *              (f32: row-major; bf16 / fp8: fragment-major, see dwdp_pack_weights)
  *              fp8 only: S13 [2I/128, H/128] and S2 [H/128, I/128] fp32 block
  *              scales, one per 128x128 block of W13 / W2 ([out, in] blocks)
  *   x_perm     [rows, H]         rows = T*k + shared*T: routed rows ordered by
@@ -205,6 +206,15 @@ size_t dwdp_expert_record_bytes(int H, int I, int w_dtype);
 /* Byte offsets of W2, S13 and S2 inside an expert record. */
 int dwdp_expert_record_offsets(int H, int I, int w_dtype, size_t* off_w2, size_t* off_s13,
                                size_t* off_s2);
+
+/* Re-lay a weight matrix w [N, K] (bf16, or fp8 E4M3 codes) into the fragment-major layout the
+ * grouped FFN reads (out: N*K elements, same size, must not alias w).  bf16 (K % 64 == 0): the
+ * 32 x 16 block (nb, kb) of W is 1 KB at byte (nb*K/16 + kb)*1024, lane l holding row 32nb + l%32,
+ * columns 16kb + 8(l/32) .. +7.  fp8 (K % 128 == 0): the 32 x 64 block (nb, kb) is 2 KB at byte
+ * (nb*K/64 + kb)*2048; lane l holds row 32nb + l%32, columns 64kb + 32(l/32) .. +31, split in two
+ * 16-byte halves at +h*1024 + 16l.  N % 32 == 0.  This is the layout of one MFMA operand per
+ * 1-2 KB, so every weight load of the GEMM is a contiguous lane-ordered 1 KB read. */
+int dwdp_pack_weights(const void* w, int64_t N, int64_t K, int dtype, void* out, void* stream);
 
 /* Block-quantise a weight matrix w [rows, cols] (fp32) to E4M3 codes q [rows, cols]
  * and fp32 scales s [rows/128, cols/128]: per 128x128 block, scale = amax/448

@@ -52,6 +52,7 @@ SIGNATURES = {
     "dwdp_expert_record_bytes": (_sz, [_i32, _i32, _i32]),
     "dwdp_expert_record_offsets": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz),
                                           ctypes.POINTER(_sz)]),
+    "dwdp_pack_weights": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "dwdp_quantize_weight_fp8": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "dwdp_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32]),
     "dwdp_last_error": (ctypes.c_char_p, []),

@@ -147,3 +147,9 @@ def table_to_device(table, device) -> torch.Tensor:
 def quantize_weight_fp8(w, q, s, stream=None):
     rows, cols = w.shape
     _lib.check(_lib.load().dwdp_quantize_weight_fp8(_ptr(w), rows, cols, _ptr(q), _ptr(s), _stream(stream)))
+
+
+def pack_weights(w, out, dtype_code_, stream=None):
+    """Re-lay a weight matrix w [N, K] (bf16, or uint8 E4M3 codes) into the fragment-major layout in out."""
+    N, K = w.shape
+    _lib.check(_lib.load().dwdp_pack_weights(_ptr(w), N, K, dtype_code_, _ptr(out), _stream(stream)))

@@ -24,6 +24,8 @@
 //   * GEMM1's weight tile holds the gate rows and the up rows of the same
 //     output columns, so SwiGLU is applied in registers in the epilogue.
 //   * f32 (small shapes only): LDS-tiled FMA kernel with the same schedule.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -425,18 +427,42 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(GemmParams p) {
     }
 }
 
-// ------------------------------------------------------------------------------ LDS-DMA kernel
+// ------------------------------------------------------------------------------ fragment kernel
 // The expert GEMMs.  One workgroup of 4 waves per CU computes a BM x 256 tile; the waves split the
-// 256 weight rows (64 each) and share all BM activation rows, so a short tail tile skips whole
-// 32-row m-blocks in every wave.  Operand slices of 128 bytes per row go straight from global
-// memory into a 3-stage LDS ring (global_load_lds_dwordx4: no register staging), two K steps
-// ahead of the MFMAs; each wave waits only for its own oldest stage (vmcnt) and one barrier per
-// step orders the ring.  XOR-swizzled 16-byte chunks keep the ds_read_b128 fragment reads
-// conflict-free.
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at lds + 16 * l
+// 256 weight rows (two 32-row n-blocks each) and share all BM activation rows, so a short tail
+// tile skips whole 32-row m-blocks in every wave.
+//   * Weights are stored fragment-major (dwdp_pack_weights): the 32 x 16 bf16 (or 32 x 64 fp8)
+//     operand of one MFMA is 1 KB (2 KB) of contiguous memory in lane order.  Each wave loads its
+//     own B fragments straight into registers with fully coalesced 16-byte loads, P = 3 K steps
+//     ahead of the MFMAs; the weights never touch LDS.
+//   * Activation rows (shared by the 4 waves) go from global memory into a (P+1)-stage LDS ring
+//     with global_load_lds_dwordx4 (no register staging); fp8 row scales ride in the same stage.
+//   * A K step is one 128-byte row slice (64 bf16 / 128 fp8); the loop is unrolled by P+1 so the
+//     ring stage and the register buffer of step kt are both compile-time (kt mod 4).  Each wave
+//     waits only for its own oldest batch (vmcnt; vector loads complete in order) and one barrier
+//     per step orders the LDS ring.
+//   * LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r sits at c ^ ((r >> 1) & 7),
+//     so the 16 lanes that ds_read_b128 serves per cycle (16 consecutive rows) hit 16 distinct
+//     16-byte slots of the 256-byte bank window.
 __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+#endif
+}
+
+// 16-byte load through the global address space (the pointer comes out of the expert table, so the
+// compiler cannot infer it; a flat load would also count against lgkmcnt and serialise with LDS)
+__device__ __forceinline__ u32x4 gload16(const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return *(const __attribute__((address_space(1))) u32x4*)p;
+#else
+    return *reinterpret_cast<const u32x4*>(p);
 #endif
 }
 
@@ -452,173 +478,214 @@ __device__ __forceinline__ void ordered_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int KIND, bool FP8>
-__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
-    constexpr int BN = 256, NW = 4, S = 3, ROWB = 128;
-    constexpr int MI = BM / 32, NJ = 2;
-    constexpr int AI = BM / 8 / NW, BI = BN / 8 / NW, PER = AI + BI;
-    constexpr int STAGE = (BM + BN) * ROWB;
-    static_assert(AI >= 1 && BM % 32 == 0, "BM must be 32, 64 or 128");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
+// Everything a tile needs once it is decoded.
+struct TileCtx {
     Tile t;
-    if (!decode_tile<BM, KIND>(p, t)) return;
+    int KT;                 // K steps
+    const uint8_t* wb[2];   // this wave's two n-block fragment streams (+ lane * 16)
+    int nblk[2];
+    const float* wscale;
+};
+
+// ROWB: bytes of one activation row per K step (64 or 128).  Weight fragments are 1 KB per 16 bf16
+// (or per 64 fp8 / 2 halves) K columns, so a step moves ROWB / 32 fragment-KB per n-block.
+template <int BM, int ROWB, bool FP8>
+struct FragCfg {
+    static constexpr int NW = 4, MI = BM / 32, NJ = 2;
+    static constexpr int CH = ROWB / 16;                      // 16-byte chunks per activation row
+    static constexpr int BF = ROWB / 32;                      // weight KB per n-block per step
+    static constexpr int AI = BM * ROWB / 1024 / NW;          // activation DMA instructions per wave per step
+    static constexpr int AS = FP8 ? (BM + 63) / 64 : 0;       // fp8 row-scale DMA instructions per wave per step
+    static constexpr int BI = NJ * BF;                        // weight DMA instructions per wave per step
+    static constexpr int PER = AI + AS + BI;                  // vector memory instructions per wave per step
+    static constexpr int ABYTES = BM * ROWB;
+    static constexpr int BBYTES = NW * BI * 1024;
+    static constexpr int STAGE = ABYTES + BBYTES + AS * 256;
+    static constexpr int NS = (147456 / STAGE) < 4 ? (147456 / STAGE) : 4;   // ring depth (<= 144 KB)
+    static constexpr int P = NS - 1;                           // steps in flight ahead of the MFMAs
+    static_assert(AI >= 1 && BM % 32 == 0 && (ROWB == 64 || ROWB == 128), "tile shape");
+    static_assert(!FP8 || ROWB == 128, "fp8 steps are one 128-wide scale block");
+    static_assert(NS >= 2 && PER * (P - 1) < 64, "ring depth / vmcnt budget");
+};
+
+// Chunk c of activation row r is stored at slot c ^ f(r) so that ds_read_b128 of 16 consecutive rows
+// (the 16 lanes one LDS cycle serves) hits 16 distinct 16-byte slots of the 256-byte bank window.
+template <int ROWB>
+__device__ __forceinline__ int aslot(int row, int chunk) {
+    return ROWB == 128 ? chunk ^ ((row >> 1) & 7) : chunk ^ ((row >> 2) & 3);
+}
+
+// Main loop and epilogue of one tile with MA active 32-row m-blocks (compile-time: the loop body is
+// straight-line code; only the LDS ring is waited on, and only here, with vmcnt).
+template <int BM, int ROWB, int MA, int KIND, bool FP8>
+__device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c, uint8_t* smem,
+                                          const float* s_bscale) {
+    using C = FragCfg<BM, ROWB, FP8>;
+    constexpr int NS = C::NS, P = C::P, NJ = C::NJ, CH = C::CH, BF = C::BF, STAGE = C::STAGE;
+    constexpr int AS = C::AS, BI = C::BI, ABYTES = C::ABYTES, BBYTES = C::BBYTES;
+    constexpr int RPI = 1024 / ROWB;                          // activation rows per DMA instruction
+    // only the first MA * 32 rows are loaded: each wave DMAs an equal share of them
+    constexpr int AI = MA * 32 / C::NW / RPI;
+    constexpr int PER = AI + AS + BI;
+    static_assert(AI >= 1 && AI * RPI * C::NW == MA * 32, "activation rows must split evenly over the waves");
+    static_assert(PER * (P - 1) < 64, "vmcnt budget");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
+    const Tile& t = c.t;
+    const int KT = c.KT;
+    const size_t lda = (size_t)p.K * (FP8 ? 1 : 2);
 
-    const uint8_t* wbase;
-    const float* wscale;
-    if (KIND == kGemm1) {
-        wbase = static_cast<const uint8_t*>(p.table[t.g].w13);
-        wscale = p.table[t.g].s13;
-    } else {
-        wbase = static_cast<const uint8_t*>(p.table[t.g].w2);
-        wscale = p.table[t.g].s2;
-    }
-    const size_t ldk = (size_t)p.K * (FP8 ? 1 : 2);
-    const int KT = p.K / (FP8 ? 128 : 64);
-
-    auto w_row = [&](int r) -> int {
-        if (KIND == kGemm1) return r < BN / 2 ? t.nt * (BN / 2) + r : p.I + t.nt * (BN / 2) + (r - BN / 2);
-        return t.nt * BN + r;
-    };
-    // tile row of the first row of this wave's n-block j (GEMM1: j = 0 gate, j = 1 up)
-    auto b_block_row = [&](int j) -> int { return KIND == kGemm1 ? j * (BN / 2) + wave * 32 : wave * 64 + j * 32; };
-    auto row_of = [&](int i, int r) -> int { return i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3); };
-
-    // lane l of a load instruction fills LDS row (l/8) position (l%8) of an 8-row group; it fetches the
-    // logical chunk that the swizzle puts there
     const uint8_t* ga[AI];
-    const uint8_t* gb[BI];
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-        const int r = (wave * AI + i) * 8 + (lane >> 3), c = (lane & 7) ^ (r & 7);
-        ga[i] = p.a + (size_t)(t.row0 + min(r, t.nrows - 1)) * ldk + c * 16;
+        const int r = (wave * AI + i) * RPI + lane / CH;
+        ga[i] = p.a + (size_t)(t.row0 + min(r, t.nrows - 1)) * lda + aslot<ROWB>(r, lane % CH) * 16;
     }
+    [[maybe_unused]] const float* gs[AS > 0 ? AS : 1];
+    if constexpr (FP8) {
+        const int KB = p.K / kFp8Group;
 #pragma unroll
-    for (int i = 0; i < BI; ++i) {
-        const int r = (wave * BI + i) * 8 + (lane >> 3), c = (lane & 7) ^ (r & 7);
-        gb[i] = wbase + (size_t)w_row(r) * ldk + c * 16;
+        for (int i = 0; i < AS; ++i) gs[i] = p.a_scale + (size_t)(t.row0 + min(i * 64 + lane, t.nrows - 1)) * KB;
     }
-    auto issue = [&](int kt) {
-        uint8_t* st = smem + (kt % S) * STAGE;
-        const size_t off = (size_t)kt * ROWB;
-#pragma unroll
-        for (int i = 0; i < AI; ++i)
-            dma16(ga[i] + off, st + (wave * AI + i) * 8 * ROWB);
-#pragma unroll
-        for (int i = 0; i < BI; ++i)
-            dma16(gb[i] + off, st + BM * ROWB + (wave * BI + i) * 8 * ROWB);
-    };
-    auto lds16 = [&](const uint8_t* base, int row, int chunk) -> u32x4 {
-        return *reinterpret_cast<const u32x4*>(base + row * ROWB + ((chunk ^ (row & 7)) << 4));
-    };
 
-    bool m_act[MI];
+    f32x16 acc[MA][NJ];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) m_act[i] = i * 32 < t.nrows;
-
-    f32x16 acc[MI][NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MA; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    issue(0);
-    if (KT > 1) issue(1);
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) wait_vmcnt<PER>();
-        else wait_vmcnt<0>();
-        ordered_barrier();
-        // fp8 scales of this K block, loaded before the next DMA batch so that waiting for them does
-        // not wait for that batch too (vector memory loads complete in order)
-        [[maybe_unused]] float sb[NJ], sa[FP8 ? MI : 1][16];
+    auto issue = [&](int kt, int buf) {
+        uint8_t* st = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < AI; ++i) dma16(ga[i] + (size_t)kt * ROWB, st + (wave * AI + i) * 1024);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int v = 0; v < BF; ++v)
+                dma16(c.wb[j] + ((size_t)kt * BF + v) * 1024, st + ABYTES + (wave * BI + j * BF + v) * 1024);
         if constexpr (FP8) {
-            const int KB = p.K / kFp8Group;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) sb[j] = wscale[(size_t)(w_row(b_block_row(j)) / kFp8Group) * KB + kt];
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    sa[i][r] = m_act[i] ? p.a_scale[(size_t)(t.row0 + min(row_of(i, r), t.nrows - 1)) * KB + kt] : 0.0f;
+            for (int i = 0; i < AS; ++i)
+                dma4(reinterpret_cast<const uint8_t*>(gs[i] + kt), st + ABYTES + BBYTES + i * 256);
         }
-        if (kt + 2 < KT) issue(kt + 2);
-        const uint8_t* A = smem + (kt % S) * STAGE;
-        const uint8_t* B = A + BM * ROWB;
+    };
+    auto a_frag = [&](const uint8_t* A, int i, int chunk) -> u32x4 {
+        const int row = i * 32 + l32;
+        return *reinterpret_cast<const u32x4*>(A + row * ROWB + (aslot<ROWB>(row, chunk) << 4));
+    };
+    auto b_frag = [&](const uint8_t* B, int j, int v) -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(B + (wave * BI + j * BF + v) * 1024 + lane * 16);
+    };
+    auto compute = [&](int kt, int buf) {
+        const uint8_t* A = smem + buf * STAGE;
+        const uint8_t* B = A + ABYTES;
         if constexpr (!FP8) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int ch = s * 2 + hi;
-                bf16x8 af[MI], bf[NJ];
+            for (int s = 0; s < ROWB / 32; ++s) {
+                bf16x8 bf[NJ];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) bf[j] = __builtin_bit_cast(bf16x8, lds16(B, b_block_row(j) + l32, ch));
+                for (int j = 0; j < NJ; ++j) bf[j] = __builtin_bit_cast(bf16x8, b_frag(B, j, s));
 #pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    if (m_act[i]) af[i] = __builtin_bit_cast(bf16x8, lds16(A, i * 32 + l32, ch));
-#pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    if (!m_act[i]) continue;
+                for (int i = 0; i < MA; ++i) {
+                    const bf16x8 af = __builtin_bit_cast(bf16x8, a_frag(A, i, s * 2 + hi));
 #pragma unroll
                     for (int j = 0; j < NJ; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[j], acc[i][j], 0, 0, 0);
                 }
             }
         } else {
-            f32x16 part[MI][NJ];
+            const float* sa_lds = reinterpret_cast<const float*>(B + BBYTES);
+            float sb[NJ];
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+            for (int j = 0; j < NJ; ++j) sb[j] = s_bscale[(wave * NJ + j) * 64 + kt];
+            i32x8 bf[NJ][2];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
+                for (int s = 0; s < 2; ++s) {
+                    const u32x4 b0 = b_frag(B, j, 2 * s), b1 = b_frag(B, j, 2 * s + 1);
+                    bf[j][s] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                                     (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+                }
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int ch = s * 4 + hi * 2;
-                i32x8 af[MI], bf[NJ];
+            for (int i = 0; i < MA; ++i) {
+                i32x8 af[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const u32x4 lo = a_frag(A, i, s * 4 + hi * 2), up = a_frag(A, i, s * 4 + hi * 2 + 1);
+                    af[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2],
+                                  (int)up[3]};
+                }
+                float sa[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *reinterpret_cast<const float4*>(sa_lds + i * 32 + q * 8 + hi * 4);
+                    sa[4 * q] = v.x;
+                    sa[4 * q + 1] = v.y;
+                    sa[4 * q + 2] = v.z;
+                    sa[4 * q + 3] = v.w;
+                }
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const int row = b_block_row(j) + l32;
-                    const u32x4 lo = lds16(B, row, ch), up = lds16(B, row, ch + 1);
-                    bf[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2],
-                                  (int)up[3]};
-                }
+                    f32x16 part;
 #pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    if (!m_act[i]) continue;
-                    const u32x4 lo = lds16(A, i * 32 + l32, ch), up = lds16(A, i * 32 + l32, ch + 1);
-                    af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2],
-                                  (int)up[3]};
-                }
+                    for (int r = 0; r < 16; ++r) part[r] = 0.0f;
 #pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    if (!m_act[i]) continue;
+                    for (int s = 0; s < 2; ++s)
+                        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[s], bf[j][s], part, 0, 0, 0, 127, 0,
+                                                                               127);
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j)
-                        part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], part[i][j], 0, 0, 0,
-                                                                                     127, 0, 127);
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += part[r] * (sa[r] * sb[j]);
                 }
             }
+        }
+    };
+
+    // prologue: batches 0 .. P-1
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                if (!m_act[i]) continue;
+    for (int u = 0; u < P; ++u)
+        if (u < KT) issue(u, u);
+    // steady state: every step of the group can issue step + P
+    int k0 = 0;
+    for (; k0 + NS + P - 1 < KT; k0 += NS) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
+        for (int u = 0; u < NS; ++u) {
+            wait_vmcnt<(P - 1) * PER>();
+            ordered_barrier();
+            issue(k0 + u + P, (u + P) % NS);
+            compute(k0 + u, u);
+        }
+    }
+    // drain: at most NS + P - 1 steps, exact waits
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) acc[i][j][r] += part[i][j][r] * (sa[i][r] * sb[j]);
+    for (int u = 0; u < NS + P - 1; ++u) {
+        const int kt = k0 + u;
+        if (kt < KT) {
+            if constexpr (P >= 2) {
+                if (kt + P - 1 < KT) wait_vmcnt<(P - 1) * PER>();
+                else if (kt + P - 2 < KT) wait_vmcnt<((P >= 3 ? P - 2 : 0)) * PER>();
+                else wait_vmcnt<0>();
+            } else {
+                wait_vmcnt<0>();
             }
+            ordered_barrier();
+            if (kt + P < KT) issue(kt + P, (u + P) % NS);
+            compute(kt, u % NS);
         }
     }
 
     // ---------------------------------------------------------------- epilogue
+    auto row_of = [&](int i, int r) -> int { return i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3); };
     if constexpr (KIND == kGemm1) {
-        const int col = t.nt * (BN / 2) + wave * 32 + l32;     // A column of this lane
+        const int col = t.nt * 128 + wave * 32 + l32;     // A column of this lane
         if constexpr (!FP8) {
             uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+            for (int i = 0; i < MA; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = row_of(i, r);
@@ -626,11 +693,11 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
                 }
         } else {
             // the tile's 128 A columns are exactly one quantisation group: amax over the 4 waves
-            ordered_barrier();                                   // the ring is free: reuse it for the reduction
+            ordered_barrier();                                   // every wave is done with the ring
             float* red = reinterpret_cast<float*>(smem);         // [NW][BM]
-            float av[MI][16];
+            float av[MA][16];
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+            for (int i = 0; i < MA; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     av[i][r] = silu_mul(acc[i][0][r], acc[i][1][r]);
@@ -642,7 +709,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
             __syncthreads();
             const int IB = p.N / kFp8Group;
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+            for (int i = 0; i < MA; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = row_of(i, r);
@@ -657,15 +724,98 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     } else {
         uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MA; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = row_of(i, r);
                     if (m < t.nrows)
-                        out[(size_t)(t.row0 + m) * p.N + t.nt * BN + wave * 64 + j * 32 + l32] = f32_to_bf16(acc[i][j][r]);
+                        out[(size_t)(t.row0 + m) * p.N + t.nt * 256 + wave * 64 + j * 32 + l32] = f32_to_bf16(acc[i][j][r]);
                 }
+    }
+}
+
+template <int BM, int KIND, bool FP8>
+__global__ __launch_bounds__(256, 1) void gemm_frag_kernel(GemmParams p) {
+    constexpr int ROWB = (BM == 256 && !FP8) ? 64 : 128;
+    using C = FragCfg<BM, ROWB, FP8>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
+    __shared__ float s_bscale[FP8 ? C::NW * C::NJ * 64 : 1];    // fp8: weight block scales (K / 128 <= 64)
+
+    TileCtx c;
+    if (!decode_tile<BM, KIND>(p, c.t)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    c.KT = p.K / (FP8 ? ROWB : ROWB / 2);
+    const uint8_t* wbase;
+    if (KIND == kGemm1) {
+        wbase = static_cast<const uint8_t*>(p.table[c.t.g].w13);
+        c.wscale = p.table[c.t.g].s13;
+    } else {
+        wbase = static_cast<const uint8_t*>(p.table[c.t.g].w2);
+        c.wscale = p.table[c.t.g].s2;
+    }
+    // fragment-major weights: 4 KB per 32-row n-block per 128 bytes of K
+    const size_t nblk_bytes = (size_t)p.K * (FP8 ? 1 : 2) * 32;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        c.nblk[j] = KIND == kGemm1 ? (j == 0 ? 0 : p.I / 32) + c.t.nt * 4 + wave : c.t.nt * 8 + wave * 2 + j;
+        c.wb[j] = wbase + (size_t)c.nblk[j] * nblk_bytes + lane * 16;
+    }
+    if constexpr (FP8) {
+        const int KB = p.K / kFp8Group;
+        for (int q = lane; q < 2 * KB; q += 64) {
+            const int j = q / KB, kb = q % KB;
+            s_bscale[(wave * 2 + j) * 64 + kb] = c.wscale[(size_t)(c.nblk[j] * 32 / kFp8Group) * KB + kb];
+        }
+        __syncthreads();
+    }
+    // active 32-row m-blocks; 256-row tiles round up to even counts to bound the variants
+    const int ma = (c.t.nrows + 31) / 32;
+    if constexpr (C::MI == 1) {
+        frag_tile<BM, ROWB, 1, KIND, FP8>(p, c, smem, s_bscale);
+    } else if constexpr (C::MI == 2) {
+        if (ma <= 1) frag_tile<BM, ROWB, 1, KIND, FP8>(p, c, smem, s_bscale);
+        else frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
+    } else if constexpr (C::MI == 4) {
+        if (ma <= 1) frag_tile<BM, ROWB, 1, KIND, FP8>(p, c, smem, s_bscale);
+        else if (ma == 2) frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
+        else if (ma == 3) frag_tile<BM, ROWB, 3, KIND, FP8>(p, c, smem, s_bscale);
+        else frag_tile<BM, ROWB, 4, KIND, FP8>(p, c, smem, s_bscale);
+    } else {
+        if (ma <= 2) frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
+        else if (ma <= 4) frag_tile<BM, ROWB, 4, KIND, FP8>(p, c, smem, s_bscale);
+        else if (ma <= 6) frag_tile<BM, ROWB, 6, KIND, FP8>(p, c, smem, s_bscale);
+        else frag_tile<BM, ROWB, 8, KIND, FP8>(p, c, smem, s_bscale);
+    }
+}
+
+// ------------------------------------------------------------------------------ weight packing
+// Fragment-major layout of a weight matrix W [N, K] (N % 32 == 0):
+//   bf16 (K % 64 == 0): fragment (nb, kb) = rows 32nb..32nb+31, columns 16kb..16kb+15, 1 KB in
+//     lane order -- lane l holds row 32nb + l%32, columns 16kb + 8(l/32) .. +7 -- stored at
+//     byte (nb * K/16 + kb) * 1024.
+//   fp8 (K % 128 == 0): fragment (nb, kb) = rows 32nb.., columns 64kb..64kb+63, 2 KB: lane l holds
+//     row 32nb + l%32, columns 64kb + 32(l/32) .. +31; bytes h*16..h*16+15 of that slice sit at
+//     byte (nb * K/64 + kb) * 2048 + h * 1024 + l * 16.
+// Both give 4 KB per 32-row block per 128-byte K step, read as four 1 KB lane-ordered loads.
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ w, int64_t N, int64_t K, int fp8,
+                                                   uint8_t* __restrict__ out) {
+    const int64_t nchunks = N * K * (fp8 ? 1 : 2) / 16;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nchunks; q += stride) {
+        int64_t row, col;
+        if (!fp8) {
+            const int64_t frag = q >> 6, l = q & 63, per = K / 16;
+            row = (frag / per) * 32 + (l & 31);
+            col = (frag % per) * 16 + (l >> 5) * 8;
+            *reinterpret_cast<uint4*>(out + q * 16) = *reinterpret_cast<const uint4*>(w + (row * K + col) * 2);
+        } else {
+            const int64_t frag = q >> 7, h = (q >> 6) & 1, l = q & 63, per = K / 64;
+            row = (frag / per) * 32 + (l & 31);
+            col = (frag % per) * 64 + (l >> 5) * 32 + h * 16;
+            *reinterpret_cast<uint4*>(out + q * 16) = *reinterpret_cast<const uint4*>(w + row * K + col);
+        }
     }
 }
 
@@ -754,8 +904,8 @@ constexpr int kBmMin = 32;
 int choose_bm(int dtype, int64_t rows, int groups) {
     if (dtype == DWDP_F32) return kBmF32;
     const int64_t mean = rows / groups;
-    const int bm = mean >= 96 ? 128 : mean >= 40 ? 64 : 32;
-    return dtype == DWDP_FP8_E4M3 ? (bm > 64 ? 64 : bm) : bm;   // fp8 keeps a partial sum: 64 rows max
+    const int bm = mean >= 192 ? 256 : mean >= 96 ? 128 : mean >= 40 ? 64 : 32;
+    return dtype == DWDP_FP8_E4M3 ? (bm > 64 ? 64 : bm) : bm;   // fp8 folds a partial sum in VGPRs: 64 rows max
 }
 
 size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -805,7 +955,7 @@ void launch_f32(const GemmParams& p, int64_t tiles, hipStream_t st) {
 
 template <int BM, int KIND, bool FP8>
 void launch_dma(const GemmParams& p, int64_t tiles, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, KIND, FP8>), dim3((unsigned)xcd_grid(tiles)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_frag_kernel<BM, KIND, FP8>), dim3((unsigned)xcd_grid(tiles)), dim3(256), 0, st, p);
 }
 
 template <int BM>
@@ -876,6 +1026,7 @@ extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* tab
         DWDP_REQUIRE(H % 64 == 0 && I % 32 == 0 && H % 16 == 0 && I % 16 == 0, "f32 path needs H % 64 == 0, I % 32 == 0");
     } else {
         DWDP_REQUIRE(H % 256 == 0 && I % 128 == 0, "bf16/fp8 paths need H % 256 == 0 and I % 128 == 0");
+        if (w_dtype == DWDP_FP8_E4M3) DWDP_REQUIRE(H <= 8192 && I <= 8192, "fp8 path needs H, I <= 8192");
     }
     if (rows == 0) return DWDP_OK;
     DWDP_REQUIRE(table && offsets && x_perm && ws && (y_perm || stage == 1), "null pointer argument");
@@ -923,7 +1074,8 @@ extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* tab
         if (g2) launch_f32<kGemm2>(p2, maxm * p2.NT, st);
     } else {
         const bool fp8 = w_dtype == DWDP_FP8_E4M3;
-        if (bm == 128 && !fp8) launch_ffn<128>(g1, g2, false, offsets, n_groups, p1, p2, maxm, st);
+        if (bm == 256 && !fp8) launch_ffn<256>(g1, g2, false, offsets, n_groups, p1, p2, maxm, st);
+        else if (bm == 128 && !fp8) launch_ffn<128>(g1, g2, false, offsets, n_groups, p1, p2, maxm, st);
         else if (bm == 64) launch_ffn<64>(g1, g2, fp8, offsets, n_groups, p1, p2, maxm, st);
         else launch_ffn<32>(g1, g2, fp8, offsets, n_groups, p1, p2, maxm, st);
     }
@@ -936,4 +1088,19 @@ extern "C" int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups,
                                     int w_dtype, void* y_perm, void* ws, size_t ws_bytes, void* stream) {
     return dwdp_moe_grouped_ffn_stage(0, table, n_groups, offsets, x_perm, x_perm_scale, rows, H, I, w_dtype, y_perm,
                                       ws, ws_bytes, stream);
+}
+
+extern "C" int dwdp_pack_weights(const void* w, int64_t N, int64_t K, int dtype, void* out, void* stream) {
+    clear_error();
+    DWDP_REQUIRE(dtype == DWDP_BF16 || dtype == DWDP_FP8_E4M3, "dtype must be DWDP_BF16 or DWDP_FP8_E4M3");
+    DWDP_REQUIRE(N > 0 && K > 0 && N % 32 == 0, "N must be a positive multiple of 32");
+    DWDP_REQUIRE(K % (dtype == DWDP_BF16 ? 64 : 128) == 0, "K must be a multiple of 64 (bf16) or 128 (fp8)");
+    DWDP_REQUIRE(w && out && w != out, "w and out must be distinct non-null pointers");
+    DWDP_REQUIRE(aligned16(w) && aligned16(out), "w and out must be 16-byte aligned");
+    const int64_t chunks = N * K * (dtype == DWDP_BF16 ? 2 : 1) / 16;
+    const int64_t grid = std::min<int64_t>((chunks + 255) / 256, 65536);
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
+                       static_cast<const uint8_t*>(w), N, K, dtype == DWDP_FP8_E4M3 ? 1 : 0, static_cast<uint8_t*>(out));
+    DWDP_LAUNCHED();
+    return DWDP_OK;
 }

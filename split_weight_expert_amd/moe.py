@@ -47,13 +47,15 @@ class ExpertStore:
         return self.buffers[buf].data_ptr() + slot * self.rec
 
     def views(self, buf: int, slot: int):
-        """(W13, W2, S13, S2) tensor views of one record (S* are None unless fp8)."""
+        """(W13, W2, S13, S2) byte regions of one record (S* are None unless fp8).
+
+        f32 weights are row-major; bf16 and fp8 weights are fragment-major (dwdp_pack_weights).
+        """
         r = self.record(buf, slot)
         H, I = self.H, self.I
-        dt = _ACT_TORCH[self.w_dtype]
-        eb = torch.tensor([], dtype=dt).element_size()
-        w13 = r[:2 * I * H * eb].view(dt).view(2 * I, H)
-        w2 = r[self.off_w2:self.off_w2 + H * I * eb].view(dt).view(H, I)
+        eb = {F32: 4, BF16: 2, FP8_E4M3: 1}[self.w_dtype]
+        w13 = r[:2 * I * H * eb]
+        w2 = r[self.off_w2:self.off_w2 + H * I * eb]
         if self.w_dtype != FP8_E4M3:
             return w13, w2, None, None
         s13 = r[self.off_s13:self.off_s13 + (2 * I // 128) * (H // 128) * 4].view(torch.float32).view(2 * I // 128,
@@ -62,15 +64,23 @@ class ExpertStore:
         return w13, w2, s13, s2
 
     def load(self, buf: int, slot: int, wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tensor, stream=None):
-        """Place one expert's weights (device tensors; fp32 masters for fp8) into a record."""
+        """Place one expert's weights ([out, in] device tensors; fp32 masters for fp8) into a record."""
         w13, w2, s13, s2 = self.views(buf, slot)
-        if self.w_dtype == FP8_E4M3:
-            api.quantize_weight_fp8(torch.cat([wg, wu], 0).float().contiguous(), w13, s13, stream)
-            api.quantize_weight_fp8(wd.float().contiguous(), w2, s2, stream)
+        H, I = self.H, self.I
+        if self.w_dtype == F32:
+            w13.view(torch.float32).view(2 * I, H)[:I].copy_(wg)
+            w13.view(torch.float32).view(2 * I, H)[I:].copy_(wu)
+            w2.view(torch.float32).view(H, I).copy_(wd)
+        elif self.w_dtype == BF16:
+            api.pack_weights(torch.cat([wg, wu], 0).to(torch.bfloat16).contiguous(), w13, BF16, stream)
+            api.pack_weights(wd.to(torch.bfloat16).contiguous(), w2, BF16, stream)
         else:
-            w13[:self.I].copy_(wg)
-            w13[self.I:].copy_(wu)
-            w2.copy_(wd)
+            q13 = torch.empty(2 * I, H, dtype=torch.uint8, device=w13.device)
+            q2 = torch.empty(H, I, dtype=torch.uint8, device=w13.device)
+            api.quantize_weight_fp8(torch.cat([wg, wu], 0).float().contiguous(), q13, s13, stream)
+            api.quantize_weight_fp8(wd.float().contiguous(), q2, s2, stream)
+            api.pack_weights(q13, w13, FP8_E4M3, stream)
+            api.pack_weights(q2, w2, FP8_E4M3, stream)
 
     def table(self, placement, device="cuda") -> torch.Tensor:
         """Device pointer table for placement = [(buffer, slot) for each group]."""

@@ -13,8 +13,6 @@ import torch
 import synth
 from synth import gen
 
-from . import api
-from ._lib import FP8_E4M3
 from .moe import DTYPES, ExpertStore, MoEBlock, act_dtype, dwdp_placement
 
 
@@ -70,22 +68,14 @@ class DeviceLayer:
         kg, ku, kd = gen.expert_keys(cfg, expert, layer)
         sg, su, sd = gen.expert_stds(cfg)
         st = torch.cuda.current_stream(self.device)
-        if self.w_dtype == FP8_E4M3:
-            w13 = torch.empty(2 * I, H, dtype=torch.float32, device=self.device)
-            wd = torch.empty(H, I, dtype=torch.float32, device=self.device)
-            _fill(kg, I * H, sg, "f32", w13.data_ptr(), st)
-            _fill(ku, I * H, su, "f32", w13.data_ptr() + I * H * 4, st)
-            _fill(kd, H * I, sd, "f32", wd.data_ptr(), st)
-            w13v, w2v, s13v, s2v = store.views(buf, slot)
-            api.quantize_weight_fp8(w13, w13v, s13v)
-            api.quantize_weight_fp8(wd, w2v, s2v)
-        else:
-            kind = gen.expert_kind(cfg)
-            eb = 4 if kind == "f32" else 2
-            base = store.record_ptr(buf, slot)
-            _fill(kg, I * H, sg, kind, base, st)
-            _fill(ku, I * H, su, kind, base + I * H * eb, st)
-            _fill(kd, H * I, sd, kind, base + store.off_w2, st)
+        kind = gen.expert_kind(cfg)
+        dt = torch.float32 if kind == "f32" else torch.bfloat16
+        w13 = torch.empty(2 * I, H, dtype=dt, device=self.device)
+        wd = torch.empty(H, I, dtype=dt, device=self.device)
+        _fill(kg, I * H, sg, kind, w13.data_ptr(), st)
+        _fill(ku, I * H, su, kind, w13.data_ptr() + I * H * w13.element_size(), st)
+        _fill(kd, H * I, sd, kind, wd.data_ptr(), st)
+        store.load(buf, slot, w13[:I], w13[I:], wd)
 
     def table(self, slot_set: int = 1) -> torch.Tensor:
         c = self.cfg

@@ -219,6 +219,9 @@ def test_weight_block_quantisation_is_bit_exact():
 
 FFN_CASES = {
     "f32": ("tiny_f32", dict(T=200)),
+    # mean rows per group picks the tile height: ~66 -> 64, ~150 -> 128, ~300 -> 256 (bf16)
+    "bf16_bm128": ("prefill8k_bf16", dict(T=300, H=512, I=256, E=4, k=2, n_local=2)),
+    "bf16_bm256": ("prefill8k_bf16", dict(T=650, H=768, I=384, E=4, k=2, n_local=2)),
     "bf16": ("prefill8k_bf16", dict(T=200, H=512, I=256, E=8, k=2, n_local=4)),
     "fp8": ("prefill16k_fp8", dict(T=200, H=512, I=256, E=8, k=2, n_local=4)),
 }
@@ -231,10 +234,11 @@ def skew_bias(E):
     return b
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16", "fp8"])
-def test_grouped_ffn_parity(dt):
+@pytest.mark.parametrize("case", ["f32", "bf16", "fp8", "bf16_bm128", "bf16_bm256"])
+def test_grouped_ffn_parity(case):
     from split_weight_expert_amd import MoEBlock
-    name, kw = FFN_CASES[dt]
+    name, kw = FFN_CASES[case]
+    dt = case.split("_")[0]
     cfg = shrink(synth.get_config(name), **kw)
     h = HostLayer(cfg, bias=skew_bias(cfg.E))
     pl, slots = placement_split(cfg)
@@ -249,6 +253,7 @@ def test_grouped_ffn_parity(dt):
     ps = bb.perm_src.cpu().numpy()
     counts = np.diff(off)
     assert counts[0] > 128 and counts[cfg.E - 1] == 0
+    assert cfg.rows // (cfg.E + cfg.shared) >= {"bf16_bm128": 96, "bf16_bm256": 192}.get(case, 0)
     y_perm = to_np(bb.y_perm).astype(np.float64)
     ws = list(h.experts) + ([h.shared] if h.shared is not None else [])
     ref = np.zeros_like(y_perm)
@@ -258,7 +263,7 @@ def test_grouped_ffn_parity(dt):
         if r1 > r0:
             wg, wu, wd = omoe.prepare_weights(*ws[g], cfg.dtype)
             ref[r0:r1] = omoe.expert_ffn(X[r0:r1], wg, wu, wd, cfg.dtype)
-    assert_close(y_perm, ref, dt, f"grouped ffn {dt}")
+    assert_close(y_perm, ref, dt, f"grouped ffn {case}")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "fp8"])
@@ -403,3 +408,36 @@ def test_prefetch_waits_for_the_last_reader():
     torch.cuda.synchronize()
     assert int(snap.max()) == 0                             # the reader saw the old contents
     assert int(dst.min()) == 3                              # and the copy then completed
+
+
+# --------------------------------------------------------------------------------------- weight layout
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_pack_weights_matches_the_documented_layout(dt):
+    from split_weight_expert_amd import api
+    rng = np.random.default_rng(21)
+    N, K = 96, 384
+    if dt == "bf16":
+        w = rng.integers(0, 2 ** 16, size=(N, K), dtype=np.uint16)
+        wt = torch.from_numpy(w.view(np.int16)).to(DEV).view(torch.bfloat16)
+        out = torch.empty_like(wt)
+        api.pack_weights(wt, out, api.BF16)
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, 8)
+        q = np.arange(N * K // 8)
+        frag, l, per = q // 64, q % 64, K // 16
+        rows = (frag // per) * 32 + l % 32
+        cols = (frag % per) * 16 + (l // 32) * 8
+        exp = np.stack([w[rows, cols + e] for e in range(8)], axis=1)
+    else:
+        w = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+        wt = torch.from_numpy(w).to(DEV)
+        out = torch.empty_like(wt)
+        api.pack_weights(wt, out, api.FP8_E4M3)
+        got = out.cpu().numpy().reshape(-1, 16)
+        q = np.arange(N * K // 16)
+        frag, h, l, per = q // 128, (q // 64) % 2, q % 64, K // 64
+        rows = (frag // per) * 32 + l % 32
+        cols = (frag % per) * 64 + (l // 32) * 32 + h * 16
+        exp = np.stack([w[rows, cols + e] for e in range(16)], axis=1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got, exp)
