@@ -496,19 +496,29 @@ struct FragCfg {
     static constexpr int NW = 4, MI = BM / 32, NJ = 2;
     static constexpr int CH = ROWB / 16;                      // 16-byte chunks per activation row
     static constexpr int BF = ROWB / 32;                      // weight KB per n-block per step
-    static constexpr int AI = BM * ROWB / 1024 / NW;          // activation DMA instructions per wave per step
+    static constexpr int RPI = 1024 / ROWB;                   // activation rows per DMA instruction
     static constexpr int AS = FP8 ? (BM + 63) / 64 : 0;       // fp8 row-scale DMA instructions per wave per step
     static constexpr int BI = NJ * BF;                        // weight DMA instructions per wave per step
-    static constexpr int PER = AI + AS + BI;                  // vector memory instructions per wave per step
     static constexpr int ABYTES = BM * ROWB;
     static constexpr int BBYTES = NW * BI * 1024;
     static constexpr int STAGE = ABYTES + BBYTES + AS * 256;
-    static constexpr int NS = (147456 / STAGE) < 4 ? (147456 / STAGE) : 4;   // ring depth (<= 144 KB)
-    static constexpr int P = NS - 1;                           // steps in flight ahead of the MFMAs
-    static_assert(AI >= 1 && BM % 32 == 0 && (ROWB == 64 || ROWB == 128), "tile shape");
+    static constexpr int EXTRA = FP8 ? NW * NJ * 64 * 4 : 0;  // fp8: weight block scales (K / 128 <= 64)
+    static constexpr int FIT = (163840 - EXTRA) / STAGE;
+    static constexpr int NS = FIT < 8 ? FIT : 8;              // ring slots
+    // bf16 reuses a slot one step after its last read (P = NS - 2), so the DMA can be issued before
+    // the step's closing LDS wait; fp8 reuses it right after the barrier (P = NS - 1)
+    static constexpr int P = FP8 ? NS - 1 : NS - 2;           // steps in flight ahead of the MFMAs
+    static_assert(BM % 32 == 0 && (ROWB == 64 || ROWB == 128), "tile shape");
     static_assert(!FP8 || ROWB == 128, "fp8 steps are one 128-wide scale block");
-    static_assert(NS >= 2 && PER * (P - 1) < 64, "ring depth / vmcnt budget");
+    static_assert(P >= 1, "ring too shallow");
 };
+
+// activation rows a tile with MA active m-blocks loads (a whole number of DMA instructions per wave)
+template <int ROWB, int MA>
+constexpr int loaded_rows() {
+    constexpr int unit = 4 * (1024 / ROWB);
+    return ((MA * 32 + unit - 1) / unit) * unit;
+}
 
 // Chunk c of activation row r is stored at slot c ^ f(r) so that ds_read_b128 of 16 consecutive rows
 // (the 16 lanes one LDS cycle serves) hits 16 distinct 16-byte slots of the 256-byte bank window.
@@ -525,12 +535,12 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     using C = FragCfg<BM, ROWB, FP8>;
     constexpr int NS = C::NS, P = C::P, NJ = C::NJ, CH = C::CH, BF = C::BF, STAGE = C::STAGE;
     constexpr int AS = C::AS, BI = C::BI, ABYTES = C::ABYTES, BBYTES = C::BBYTES;
-    constexpr int RPI = 1024 / ROWB;                          // activation rows per DMA instruction
-    // only the first MA * 32 rows are loaded: each wave DMAs an equal share of them
-    constexpr int AI = MA * 32 / C::NW / RPI;
+    constexpr int RPI = C::RPI;
+    // only the rows of the MA active m-blocks are loaded: each wave DMAs an equal share of them
+    constexpr int AI = loaded_rows<ROWB, MA>() / C::NW / RPI;
     constexpr int PER = AI + AS + BI;
-    static_assert(AI >= 1 && AI * RPI * C::NW == MA * 32, "activation rows must split evenly over the waves");
-    static_assert(PER * (P - 1) < 64, "vmcnt budget");
+    static_assert(AI >= 1 && loaded_rows<ROWB, MA>() <= BM, "activation rows must split evenly over the waves");
+    static_assert(PER * P < 64, "vmcnt budget");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
     const Tile& t = c.t;
@@ -645,36 +655,118 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         }
     };
 
-    // prologue: batches 0 .. P-1
+    if constexpr (!FP8) {
+        // bf16: fragments of the next sub-step are read from LDS while the MFMAs of the current one
+        // run; the last sub-step of a step first crosses the barrier into the next step's slot.
+        constexpr int S = ROWB / 32;
+        struct Frags {
+            bf16x8 a[MA];
+            bf16x8 b[NJ];
+        };
+        Frags F[2];
+        auto load = [&](Frags& f, int buf, int sub) {
+            const uint8_t* A = smem + buf * STAGE;
+            const uint8_t* B = A + ABYTES;
 #pragma unroll
-    for (int u = 0; u < P; ++u)
-        if (u < KT) issue(u, u);
-    // steady state: every step of the group can issue step + P
-    int k0 = 0;
-    for (; k0 + NS + P - 1 < KT; k0 += NS) {
+            for (int j = 0; j < NJ; ++j) f.b[j] = __builtin_bit_cast(bf16x8, b_frag(B, j, sub));
 #pragma unroll
-        for (int u = 0; u < NS; ++u) {
-            wait_vmcnt<(P - 1) * PER>();
-            ordered_barrier();
-            issue(k0 + u + P, (u + P) % NS);
-            compute(k0 + u, u);
-        }
-    }
-    // drain: at most NS + P - 1 steps, exact waits
+            for (int i = 0; i < MA; ++i) f.a[i] = __builtin_bit_cast(bf16x8, a_frag(A, i, sub * 2 + hi));
+        };
+        auto mma = [&](const Frags& f) {
 #pragma unroll
-    for (int u = 0; u < NS + P - 1; ++u) {
-        const int kt = k0 + u;
-        if (kt < KT) {
-            if constexpr (P >= 2) {
-                if (kt + P - 1 < KT) wait_vmcnt<(P - 1) * PER>();
-                else if (kt + P - 2 < KT) wait_vmcnt<((P >= 3 ? P - 2 : 0)) * PER>();
-                else wait_vmcnt<0>();
+            for (int i = 0; i < MA; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        };
+        // End of step kt (ring slot u) into step kt + 1.  Batch kt + 1 + P goes to the slot of step
+        // kt - 1, which every wave stopped reading before the previous barrier; issuing it here, just
+        // before the LDS wait, keeps the compiler's ds_read counting exact after the barrier.
+        auto cross = [&](int kt, int u, bool steady) {
+            __builtin_amdgcn_sched_barrier(0);   // keep the DMA (it rewrites M0) out of the MFMA region
+            if (steady || kt + 1 + P < KT) issue(kt + 1 + P, (u + 1 + P) % NS);
+            __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
+            // batch kt + 1 must have landed: the batches after it are kt+2 .. min(KT-1, kt+1+P)
+            if (steady) {
+                wait_vmcnt<P * PER>();
             } else {
-                wait_vmcnt<0>();
+                const int after = min(KT - 2 - kt, P);
+                if (after >= P) wait_vmcnt<P * PER>();
+                else if (P >= 2 && after == P - 1) wait_vmcnt<(P >= 2 ? P - 1 : 0) * PER>();
+                else if (P >= 3 && after == P - 2) wait_vmcnt<(P >= 3 ? P - 2 : 0) * PER>();
+                else wait_vmcnt<0>();
             }
             ordered_barrier();
-            if (kt + P < KT) issue(kt + P, (u + P) % NS);
-            compute(kt, u % NS);
+            load(F[0], (u + 1) % NS, 0);
+        };
+        // Interleave the next fragments' ds_reads one by one between this sub-step's MFMAs: the LDS
+        // counter is 4 bits, so a batch of reads issued ahead of still-pending ones would force a
+        // full drain (lgkmcnt(0)) before the first MFMA.
+        constexpr int NL = MA + NJ, NM = MA * NJ, PERL = (NM + NL - 1) / NL;
+        auto interleave = [&]() {
+#pragma unroll
+            for (int q = 0; q < NL; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, PERL, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+            }
+        };
+        auto step = [&](int kt, int u, bool steady) {
+#pragma unroll
+            for (int sub = 0; sub < S; ++sub) {
+                if (sub + 1 < S) load(F[(sub + 1) & 1], u, sub + 1);
+                else if (steady || kt + 1 < KT) cross(kt, u, steady);
+                mma(F[sub & 1]);
+                interleave();
+            }
+        };
+        // prologue: batches 0 .. P into slots 0 .. P
+#pragma unroll
+        for (int u = 0; u <= P; ++u)
+            if (u < KT) issue(u, u);
+        if (KT > P) wait_vmcnt<P * PER>();               // batch 0 landed (1 .. P may be in flight)
+        else wait_vmcnt<0>();
+        ordered_barrier();
+        load(F[0], 0, 0);
+        int k0 = 0;
+        for (; k0 + NS + P < KT; k0 += NS) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u) step(k0 + u, u, true);
+        }
+#pragma unroll
+        for (int u = 0; u < NS + P; ++u)
+            if (k0 + u < KT) step(k0 + u, u % NS, false);
+    } else {
+        // prologue: batches 0 .. P-1
+#pragma unroll
+        for (int u = 0; u < P; ++u)
+            if (u < KT) issue(u, u);
+        // steady state: every step of the group can issue step + P
+        int k0 = 0;
+        for (; k0 + NS + P - 1 < KT; k0 += NS) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u) {
+                wait_vmcnt<(P - 1) * PER>();
+                ordered_barrier();
+                issue(k0 + u + P, (u + P) % NS);
+                compute(k0 + u, u);
+            }
+        }
+        // drain: at most NS + P - 1 steps, exact waits
+#pragma unroll
+        for (int u = 0; u < NS + P - 1; ++u) {
+            const int kt = k0 + u;
+            if (kt < KT) {
+                if constexpr (P >= 2) {
+                    if (kt + P - 1 < KT) wait_vmcnt<(P - 1) * PER>();
+                    else if (kt + P - 2 < KT) wait_vmcnt<((P >= 3 ? P - 2 : 0)) * PER>();
+                    else wait_vmcnt<0>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                ordered_barrier();
+                if (kt + P < KT) issue(kt + P, (u + P) % NS);
+                compute(kt, u % NS);
+            }
         }
     }
 
@@ -738,10 +830,10 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
 
 template <int BM, int KIND, bool FP8>
 __global__ __launch_bounds__(256, 1) void gemm_frag_kernel(GemmParams p) {
-    constexpr int ROWB = (BM == 256 && !FP8) ? 64 : 128;
+    constexpr int ROWB = (FP8 || BM == 32) ? 128 : 64;
     using C = FragCfg<BM, ROWB, FP8>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
-    __shared__ float s_bscale[FP8 ? C::NW * C::NJ * 64 : 1];    // fp8: weight block scales (K / 128 <= 64)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE + C::EXTRA];
+    float* s_bscale = reinterpret_cast<float*>(smem + C::NS * C::STAGE);   // fp8 only
 
     TileCtx c;
     if (!decode_tile<BM, KIND>(p, c.t)) return;
