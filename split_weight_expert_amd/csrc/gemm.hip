@@ -72,6 +72,16 @@ struct Tile {
     int nrows;
 };
 
+// Tiles reach the XCDs in clusters: workgroup b runs on XCD b % 8, and XCD x takes clusters x, x+8,
+// x+16, ... of kCluster consecutive tiles, in order.  Consecutive tiles share operands (below), so a
+// cluster's reuse stays inside one XCD's L2, while the round-robin over clusters spreads heavy and
+// light groups evenly over the eight XCDs.
+constexpr int kCluster = 32;
+// Inside a group, m-tiles are taken in super-blocks of up to kMSuper: the tiles of a super-block run
+// n-tile by n-tile with the m-tiles innermost, so a window of 32 running tiles reads about 4
+// activation slabs and 8 weight slabs instead of 32 of one kind.
+constexpr int kMSuper = 4;
+
 template <int BM, int KIND>
 __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
     int total;
@@ -82,11 +92,9 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
     } else {
         total = p.mprefix[p.G] * p.NT;
     }
-    const int per = (total + kNumXcd - 1) / kNumXcd;
     const int bid = blockIdx.x;
     const int slot = bid / kNumXcd;
-    if (slot >= per) return false;
-    const int lin = (bid % kNumXcd) * per + slot;
+    const int lin = ((slot / kCluster) * kNumXcd + bid % kNumXcd) * kCluster + slot % kCluster;
     if (lin >= total) return false;
     if (KIND == kRouter) {
         const int mi = lin % mt_router;
@@ -97,10 +105,13 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
         return true;
     }
     const MTile m = p.mtiles[lin / p.NT];
-    const int rem = lin - m.m0 * p.NT;
+    int rem = lin - m.m0 * p.NT;               // tile index inside the group
+    const int sb = rem / (kMSuper * p.NT);     // m super-block
+    const int ms = min(kMSuper, m.mc - sb * kMSuper);
+    rem -= sb * kMSuper * p.NT;
     t.g = m.g;
-    t.nt = rem / m.mc;
-    const int mi = rem - t.nt * m.mc;
+    t.nt = rem / ms;
+    const int mi = sb * kMSuper + rem % ms;
     const int r0 = p.offsets[m.g], r1 = p.offsets[m.g + 1];
     t.row0 = (int64_t)r0 + (int64_t)mi * BM;
     t.nrows = min(BM, r1 - (int)t.row0);
@@ -1030,9 +1041,12 @@ void launch_schedule(const int32_t* offsets, int G, int32_t* pre, MTile* mt, hip
     hipLaunchKernelGGL(schedule_kernel<BM>, dim3(1), dim3(1024), 0, st, offsets, G, pre, mt);
 }
 
-// decode_tile gives XCD x the slots x, x+8, x+16, ... of a stretch of ceil(total/8) tiles, so the
-// launch must hold whole rounds of 8 workgroups: round the tile bound up to a multiple of 8.
-int64_t xcd_grid(int64_t tiles) { return (tiles + kNumXcd - 1) / kNumXcd * kNumXcd; }
+// decode_tile deals clusters of kCluster tiles round-robin over the 8 XCDs, so the launch holds whole
+// rounds of 8 clusters: round the tile bound up to a multiple of 8 * kCluster (the surplus exits).
+int64_t xcd_grid(int64_t tiles) {
+    constexpr int64_t q = (int64_t)kNumXcd * kCluster;
+    return (tiles + q - 1) / q * q;
+}
 
 template <int BM, int BN, int WM, int WN, int KIND, bool FP8>
 void launch_mfma(const GemmParams& p, int64_t tiles, hipStream_t st) {
