@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill8k_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=6, help="experts whose rows the oracle's sample covers")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="FFN seconds the oracle's timed sample covers")
     ap.add_argument("--no-prefetch", action="store_true", help="skip the prefetch / overlap measurement")
     ap.add_argument("--copy-workgroups", type=int, default=32)
     ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy"])
@@ -74,12 +74,13 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, n_experts):
+def cpu_baseline(cfg, budget_s):
     """The oracle (as it stands) on a bounded sample of the workload, scaled to the whole layer.
 
     Sample: routing and permutation of all T tokens, then the expert FFN of every row routed to
-    the first `n_experts` experts that received rows.  The FFN time is scaled by total rows /
-    sampled rows (the FFN is over 99% of the layer's FLOPs).  Weight generation is not timed.
+    experts 0, 1, 2, ... (in order, skipping empty ones) until `budget_s` seconds of FFN work have
+    been timed.  The FFN time is scaled by total rows / sampled rows (the FFN is over 99% of the
+    layer's FLOPs).  Weight generation is not timed.
     """
     import threadpoolctl
 
@@ -93,9 +94,12 @@ def cpu_baseline(cfg, n_experts):
     logits, idx, w = omoe.route(x, wr, b, cfg.k)
     offsets, src, inv, counts = omoe.permute(idx, cfg.E, cfg.shared)
     t_route = time.perf_counter() - t0
-    chosen = [e for e in range(cfg.E) if counts[e] > 0][:n_experts]
-    t_ffn, rows = 0.0, 0
-    for e in chosen:
+    t_ffn, rows, chosen = 0.0, 0, []
+    for e in range(cfg.E):
+        if t_ffn >= budget_s:
+            break
+        if counts[e] == 0:
+            continue
         wts = synth.expert_weights(cfg, e)
         r0, r1 = offsets[e], offsets[e + 1]
         t0 = time.perf_counter()
@@ -104,16 +108,72 @@ def cpu_baseline(cfg, n_experts):
         omoe.expert_ffn(X, wg, wu, wd, cfg.dtype)
         t_ffn += time.perf_counter() - t0
         rows += int(r1 - r0)
+        chosen.append(e)
     total_rows = cfg.T * (cfg.k + cfg.shared)
     est = t_route + t_ffn * total_rows / rows
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     return dict(value=cfg.T / est, unit="tokens/s", cores=int(threads), kind="oracle",
                 tflops=6 * cfg.H * cfg.I * total_rows / est / 1e12,
-                sample=(f"routing + permutation of all {cfg.T} tokens ({t_route:.2f} s) and the fp64 expert FFN "
-                        f"of the {rows} rows routed to experts {chosen[0]}..{chosen[-1]} ({t_ffn:.2f} s), "
-                        f"FFN time scaled by {total_rows}/{rows} rows to the whole layer; "
-                        f"weight generation not timed"))
+                sample=(f"routing + permutation of all {cfg.T} tokens ({t_route:.2f} s) and the {cfg.dtype}-policy "
+                        f"fp64 expert FFN of the {rows} rows routed to the {len(chosen)} non-empty experts among "
+                        f"0..{chosen[-1]} ({t_ffn:.2f} s), FFN time scaled by {total_rows}/{rows} rows to the "
+                        f"whole layer; weight generation not timed"))
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    with open(os.path.join(ROOT, "split_weight_expert_amd", "csrc", "gemm.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM1 launch from the committed counter summary, if it was taken on this kernel source.
+
+    The summary (profiles/gemm1_<workload>_hbm_traffic.md) holds FETCH_SIZE + WRITE_SIZE per dispatch,
+    each scaled by what the counter reads for a copy of known size, and the sha256 of gemm.hip at the
+    time; a different source gives None.
+    """
+    import re
+    path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", text)
+    v = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not h or not v or h.group(1) != gemm_source_hash():
+        return None
+    return int(v.group(1))
+
+
+def roofline(cfg, g1_ms, rows, touched, peak):
+    """Roofline of the dominant kernel, GEMM1 + SwiGLU (gemm_frag_kernel, 2/3 of the FLOPs and weight bytes).
+
+    Algorithmic work per launch: 4*H*I FLOPs per permuted row, and the W13 record part of every touched
+    group read once (weights only; permuted activations are implementation traffic).  Decode batches
+    (fewer rows than 8 per expert) are bounded by HBM, prefill by the MFMA peak of the weight dtype;
+    both fractions are reported.
+    """
+    g1_s = g1_ms / 1e3
+    flops = 4 * cfg.H * cfg.I * rows
+    eb = {"fp8": 1, "bf16": 2, "f32": 4}[cfg.dtype]
+    wbytes = touched * 2 * cfg.I * cfg.H * eb
+    if cfg.dtype == "fp8":
+        wbytes += touched * (2 * cfg.I // 128) * (cfg.H // 128) * 4
+    hbm = dict(achieved=wbytes / g1_s / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s")
+    mfma = dict(achieved=flops / g1_s / 1e12, peak=peak / 1e12, unit="TFLOP/s")
+    decode = cfg.T * cfg.k < cfg.E * 8
+    main_, other = (hbm, mfma) if decode else (mfma, hbm)
+    roof = dict(bound="hbm" if decode else "mfma", **main_)
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    traffic = measured_traffic(cfg.name)
+    roof["traffic"] = traffic
+    roof["kernel"] = "gemm_frag_kernel, GEMM1 + SwiGLU epilogue"
+    roof["algorithmic"] = dict(flops=flops, weight_bytes=wbytes)
+    roof["other_bound"] = dict(bound="mfma" if decode else "hbm", **other, frac=other["achieved"] / other["peak"])
+    if traffic:
+        roof["traffic_over_algorithmic_bytes"] = traffic / wbytes
+    return roof
 
 
 def main():
@@ -187,19 +247,7 @@ def main():
     flops_total = flops_ffn + 2 * cfg.T * cfg.H * cfg.E
     peak = {"bf16": PEAK_BF16, "fp8": PEAK_FP8, "f32": PEAK_FP32}[cfg.dtype]
     wbytes = layer.store.rec
-    # the dominant kernel is GEMM1 + SwiGLU (2/3 of the FLOPs, 2/3 of the weight bytes)
-    g1_s = stage_ms["gemm1_swiglu"] / 1e3
-    g1_flops = 4 * cfg.H * cfg.I * rows
-    g1_bytes = touched * (2 * cfg.I * cfg.H) * (1 if cfg.dtype == "fp8" else 2 if cfg.dtype == "bf16" else 4)
-    decode = cfg.T * cfg.k < cfg.E * 8
-    if decode:
-        roof = dict(bound="hbm", achieved=g1_bytes / g1_s / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s")
-    else:
-        roof = dict(bound="mfma", achieved=g1_flops / g1_s / 1e12, peak=peak / 1e12, unit="TFLOP/s")
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "gemm_mfma_kernel (GEMM1 + SwiGLU epilogue)"
-
+    res_roof = roofline(cfg, stage_ms["gemm1_swiglu"], rows, touched, peak)
     res = dict(metric=METRIC, value=cfg.T / (ms_step / 1e3), unit="tokens/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=ms_step, higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype=cfg.dtype, data="synthetic (seeded; no trained weights)",
@@ -210,14 +258,14 @@ def main():
                tflops_ffn=flops_ffn / ((stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) / 1e3) / 1e12,
                frac_peak_ffn=flops_ffn / ((stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) / 1e3) / peak,
                weight_gbps_ffn=touched * wbytes / ((stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) / 1e3) / 1e9,
-               experts_touched=touched, rows=rows, stage_ms=stage_ms, roofline=roof)
+               experts_touched=touched, rows=rows, stage_ms=stage_ms, roofline=res_roof)
 
     if want_prefetch:
         res["prefetch"] = measure_prefetch(layer, block, step, args, cfg, ms_step)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_experts)
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
