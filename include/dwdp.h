@@ -152,7 +152,10 @@ int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, int shared,
  *   rows must equal offsets[n_groups] (not checked on the device).  H % 256 == 0,
  *   I % 128 == 0 (BF16/FP8); H % 4, I % 4 == 0 (F32).  offsets is read on the
  *   device only; no host synchronisation happens.
- *   ws: dwdp_workspace_bytes(DWDP_OP_GROUPED_FFN, ...) bytes (holds A). */
+ *   ws: dwdp_workspace_bytes(DWDP_OP_GROUPED_FFN, ...) bytes.  After GEMM1 it
+ *     begins with A [rows, I] row-major in the activation type (fp32, bf16, or
+ *     E4M3 codes), followed for FP8 at the next 256-byte boundary by A's scales
+ *     [rows, I/128] fp32; the tile schedule sits after them. */
 int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,
                          const void* x_perm, const float* x_perm_scale, int64_t rows, int H, int I,
                          int w_dtype, void* y_perm, void* ws, size_t ws_bytes, void* stream);

@@ -166,23 +166,35 @@ def prepare_tokens(x, precision: str) -> np.ndarray:
     return np.asarray(x, np.float64)
 
 
-def expert_ffn(X, wg, wu, wd, precision: str) -> np.ndarray:
-    """Y = W_d (silu(W_g X) * (W_u X)) for the rows of X, with the policy's rounding points.
+def expert_ffn_parts(X, wg, wu, wd, precision: str) -> dict:
+    """The expert FFN with its intermediate: Y = W_d (silu(W_g X) * (W_u X)) for the rows of X.
 
-    X and the weights are the prepared values (see prepare_tokens / prepare_weights).
+    X and the weights are the prepared values (see prepare_tokens / prepare_weights).  Returns
+    A (the intermediate as the down projection consumes it, after the policy's rounding point),
+    A_codes and A_scales (fp8 only: the E4M3 codes and group scales of A) and Y.
     """
     X = np.asarray(X, np.float64)
     G = X @ wg.T
     U = X @ wu.T
     A = silu(G) * U
+    codes = scales = None
     if precision == "bf16":
         A = bf16_round(A)
     elif precision == "fp8":
-        A = dequant_groups(*quantize_groups(A.astype(np.float32)))
+        codes, scales = quantize_groups(A.astype(np.float32))
+        A = dequant_groups(codes, scales)
     Y = A @ wd.T
     if precision in ("bf16", "fp8"):
         Y = bf16_round(Y)
-    return Y
+    return dict(A=A, A_codes=codes, A_scales=scales, Y=Y)
+
+
+def expert_ffn(X, wg, wu, wd, precision: str) -> np.ndarray:
+    """Y = W_d (silu(W_g X) * (W_u X)) for the rows of X, with the policy's rounding points.
+
+    X and the weights are the prepared values (see prepare_tokens / prepare_weights).
+    """
+    return expert_ffn_parts(X, wg, wu, wd, precision)["Y"]
 
 
 def combine(y_rows, w, shared_row=None, precision: str = "f32") -> np.ndarray:

@@ -996,8 +996,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------------------------------------ configs
-// Expert GEMMs (bf16, fp8): gemm_dma_kernel, BM x 256 tiles with BM = 32, 64 or 128 picked from the
-// mean rows per group (decode batches give groups of a few rows).  f32: 64 x 64 FMA tiles.
+// Expert GEMMs (bf16, fp8): gemm_frag_kernel, BM x 256 tiles with BM = 32, 64, 128 or 256 (fp8: at
+// most 128) picked from the mean rows per group (decode batches give groups of a few rows).
+// f32: 64 x 64 FMA tiles.
 // Router (bf16): gemm_mfma_kernel, 64 x 64 tiles.
 constexpr int kBnDma = 256;
 constexpr int kBmF32 = 64, kBnF32 = 64;
@@ -1008,7 +1009,7 @@ int choose_bm(int dtype, int64_t rows, int groups) {
     if (dtype == DWDP_F32) return kBmF32;
     const int64_t mean = rows / groups;
     const int bm = mean >= 192 ? 256 : mean >= 96 ? 128 : mean >= 40 ? 64 : 32;
-    return dtype == DWDP_FP8_E4M3 ? (bm > 64 ? 64 : bm) : bm;   // fp8 folds a partial sum in VGPRs: 64 rows max
+    return dtype == DWDP_FP8_E4M3 ? (bm > 128 ? 128 : bm) : bm;   // fp8 folds partial sums in VGPRs: 128 rows max
 }
 
 size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -1068,7 +1069,7 @@ template <int BM>
 void launch_ffn(bool g1, bool g2, bool fp8_path, const int32_t* offsets, int G, const GemmParams& p1,
                 const GemmParams& p2, int64_t maxm, hipStream_t st) {
     if (g1) launch_schedule<BM>(offsets, G, const_cast<int32_t*>(p1.mprefix), const_cast<MTile*>(p1.mtiles), st);
-    if constexpr (BM <= 64) {
+    if constexpr (BM <= 128) {
         if (fp8_path) {
             if (g1) launch_dma<BM, kGemm1, true>(p1, maxm * p1.NT, st);
             if (g2) launch_dma<BM, kGemm2, true>(p2, maxm * p2.NT, st);
@@ -1181,7 +1182,7 @@ extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* tab
     } else {
         const bool fp8 = w_dtype == DWDP_FP8_E4M3;
         if (bm == 256 && !fp8) launch_ffn<256>(g1, g2, false, offsets, n_groups, p1, p2, maxm, st);
-        else if (bm == 128 && !fp8) launch_ffn<128>(g1, g2, false, offsets, n_groups, p1, p2, maxm, st);
+        else if (bm == 128) launch_ffn<128>(g1, g2, fp8, offsets, n_groups, p1, p2, maxm, st);
         else if (bm == 64) launch_ffn<64>(g1, g2, fp8, offsets, n_groups, p1, p2, maxm, st);
         else launch_ffn<32>(g1, g2, fp8, offsets, n_groups, p1, p2, maxm, st);
     }

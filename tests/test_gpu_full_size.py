@@ -28,7 +28,7 @@ import torch
 
 import synth
 from oracle import moe as omoe
-from tests.gpu_util import assert_close, need_gpu, to_np
+from tests.gpu_util import assert_close, check_fp8_rows, ffn_ws_a, need_gpu, rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -113,9 +113,15 @@ def test_full_size_block(name, n_tokens):
         r0, r1 = int(offsets[g]), int(offsets[g + 1])
         rws = np.unique(np.linspace(r0, r1 - 1, min(8, r1 - r0)).astype(int))
         wts = omoe.prepare_weights(*synth.expert_weights(cfg, g), cfg.dtype)
-        ref_rows = omoe.expert_ffn(omoe.prepare_tokens(x[perm_src[rws]], cfg.dtype), *wts, cfg.dtype)
+        parts = omoe.expert_ffn_parts(omoe.prepare_tokens(x[perm_src[rws]], cfg.dtype), *wts, cfg.dtype)
         got = to_np(b.y_perm[torch.from_numpy(rws).cuda()])
-        mx, mn = assert_close(got, ref_rows, cfg.dtype, f"{name} group {g} rows {rws.tolist()}")
+        what = f"{name} group {g} rows {rws.tolist()}"
+        if cfg.dtype == "fp8":
+            codes, scales = ffn_ws_a(b.ws_ffn, len(perm_src), cfg.I, rws)
+            flips, mx = check_fp8_rows(got, codes, scales, parts, wts[2], np.sqrt((parts["Y"] ** 2).mean()), what)
+            mn = rel_err(got, parts["Y"])[1]
+        else:
+            mx, mn = assert_close(got, parts["Y"], cfg.dtype, what)
         print(f"[full-size] {name}: group {g} ({r1 - r0} rows) max rel {mx:.2e} mean rel {mn:.2e}", flush=True)
 
     toks = sample_tokens(idx, counts, cfg.T, n_tokens)

@@ -13,7 +13,8 @@ import synth
 from oracle import codecs, moe as omoe
 from oracle.prefetch import apply_plan
 from synth.configs import shrink
-from tests.gpu_util import HostLayer, assert_close, need_gpu, rel_err, to_np, upload_layer
+from tests.gpu_util import (TOL, HostLayer, assert_close, check_fp8_rows, ffn_ws_a, need_gpu, rel_err, to_np,
+                            upload_layer)
 
 pytestmark = pytest.mark.gpu
 
@@ -224,6 +225,7 @@ FFN_CASES = {
     "bf16_bm256": ("prefill8k_bf16", dict(T=650, H=768, I=384, E=4, k=2, n_local=2)),
     "bf16": ("prefill8k_bf16", dict(T=200, H=512, I=256, E=8, k=2, n_local=4)),
     "fp8": ("prefill16k_fp8", dict(T=200, H=512, I=256, E=8, k=2, n_local=4)),
+    "fp8_bm128": ("prefill16k_fp8", dict(T=300, H=512, I=256, E=4, k=2, n_local=2)),
 }
 
 
@@ -234,7 +236,7 @@ def skew_bias(E):
     return b
 
 
-@pytest.mark.parametrize("case", ["f32", "bf16", "fp8", "bf16_bm128", "bf16_bm256"])
+@pytest.mark.parametrize("case", ["f32", "bf16", "fp8", "bf16_bm128", "bf16_bm256", "fp8_bm128"])
 def test_grouped_ffn_parity(case):
     from split_weight_expert_amd import MoEBlock
     name, kw = FFN_CASES[case]
@@ -253,17 +255,28 @@ def test_grouped_ffn_parity(case):
     ps = bb.perm_src.cpu().numpy()
     counts = np.diff(off)
     assert counts[0] > 128 and counts[cfg.E - 1] == 0
-    assert cfg.rows // (cfg.E + cfg.shared) >= {"bf16_bm128": 96, "bf16_bm256": 192}.get(case, 0)
+    assert cfg.rows // (cfg.E + cfg.shared) >= {"bf16_bm128": 96, "bf16_bm256": 192, "fp8_bm128": 96}.get(case, 0)
     y_perm = to_np(bb.y_perm).astype(np.float64)
     ws = list(h.experts) + ([h.shared] if h.shared is not None else [])
     ref = np.zeros_like(y_perm)
     X = omoe.prepare_tokens(h.x[ps], cfg.dtype)     # fp8: the oracle's own per-token quantisation
+    parts = {}
     for g in range(len(ws)):
         r0, r1 = off[g], off[g + 1]
         if r1 > r0:
             wg, wu, wd = omoe.prepare_weights(*ws[g], cfg.dtype)
-            ref[r0:r1] = omoe.expert_ffn(X[r0:r1], wg, wu, wd, cfg.dtype)
-    assert_close(y_perm, ref, dt, f"grouped ffn {case}")
+            parts[g] = (omoe.expert_ffn_parts(X[r0:r1], wg, wu, wd, cfg.dtype), wd)
+            ref[r0:r1] = parts[g][0]["Y"]
+    if dt != "fp8":
+        assert_close(y_perm, ref, dt, f"grouped ffn {case}")
+        return
+    # fp8: A is re-quantised from fp32 values accumulated in different orders on the two sides
+    codes, scales = ffn_ws_a(bb.ws_ffn, cfg.rows, cfg.I)
+    rms = np.sqrt((ref ** 2).mean())
+    for g, (pt, wd) in parts.items():
+        r0, r1 = off[g], off[g + 1]
+        check_fp8_rows(y_perm[r0:r1], codes[r0:r1], scales[r0:r1], pt, wd, rms, f"grouped ffn {case} group {g}")
+    assert rel_err(y_perm, ref)[1] <= TOL["fp8"]["mean"]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "fp8"])
