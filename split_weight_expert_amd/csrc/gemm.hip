@@ -439,22 +439,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------------------------------------ fragment kernel
-// The expert GEMMs.  One workgroup of 4 waves per CU computes a BM x 256 tile; the waves split the
-// 256 weight rows (two 32-row n-blocks each) and share all BM activation rows, so a short tail
-// tile skips whole 32-row m-blocks in every wave.
+// The expert GEMMs.  One workgroup per CU computes a BM x 256 tile of one group.  The 256 output
+// columns are four column groups of 64 (two 32-wide n-blocks each); each column group is one wave
+// holding all BM rows (bf16), or two waves holding 64 rows each (fp8 at BM = 128).  A short tail tile
+// runs a variant that touches only its active 32-row m-blocks.
 //   * Weights are stored fragment-major (dwdp_pack_weights): the 32 x 16 bf16 (or 32 x 64 fp8)
-//     operand of one MFMA is 1 KB (2 KB) of contiguous memory in lane order.  Each wave loads its
-//     own B fragments straight into registers with fully coalesced 16-byte loads, P = 3 K steps
-//     ahead of the MFMAs; the weights never touch LDS.
-//   * Activation rows (shared by the 4 waves) go from global memory into a (P+1)-stage LDS ring
-//     with global_load_lds_dwordx4 (no register staging); fp8 row scales ride in the same stage.
-//   * A K step is one 128-byte row slice (64 bf16 / 128 fp8); the loop is unrolled by P+1 so the
-//     ring stage and the register buffer of step kt are both compile-time (kt mod 4).  Each wave
-//     waits only for its own oldest batch (vmcnt; vector loads complete in order) and one barrier
-//     per step orders the LDS ring.
-//   * LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r sits at c ^ ((r >> 1) & 7),
-//     so the 16 lanes that ds_read_b128 serves per cycle (16 consecutive rows) hit 16 distinct
-//     16-byte slots of the 256-byte bank window.
+//     operand of one MFMA is 1 KB (2 KB) of contiguous memory in lane order.
+//   * Every operand goes from global memory straight into an NS-stage LDS ring with
+//     global_load_lds_dwordx4 (no register staging): per K step the stage holds ROWB bytes of each
+//     active row, the weight fragments of all four column groups and, for fp8, the row scales.
+//     Each wave issues its own share and waits only for its own oldest batch (vmcnt; vector loads
+//     complete in order); one barrier per step orders the ring.
+//   * bf16 keeps P = NS - 2 steps in flight and issues the next batch before the step's closing LDS
+//     wait; its LDS reads are interleaved one by one with the MFMAs.  fp8 keeps P = NS - 1.
+//   * Activation rows are swizzled in LDS (aslot) so that the 16 lanes one ds_read_b128 cycle
+//     serves hit 16 distinct 16-byte slots of the 256-byte bank window.
 __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
@@ -502,16 +501,25 @@ struct TileCtx {
 
 // ROWB: bytes of one activation row per K step (64 or 128).  Weight fragments are 1 KB per 16 bf16
 // (or per 64 fp8 / 2 halves) K columns, so a step moves ROWB / 32 fragment-KB per n-block.
+//
+// Waves: four column groups of 64 output columns each.  bf16 tiles have one wave per column group
+// holding all BM rows.  fp8 tiles of 128 rows have two waves per column group, one per 64-row part
+// (two waves per SIMD), so that one wave's fp32 scale fold runs while the other's MFMAs do.
+constexpr int rowb_of(int BM, bool FP8) { return (FP8 || BM == 32) ? 128 : 64; }
+
 template <int BM, int ROWB, bool FP8>
 struct FragCfg {
-    static constexpr int NW = 4, MI = BM / 32, NJ = 2;
+    static constexpr int NW = (FP8 && BM >= 128) ? 8 : 4;    // waves
+    static constexpr int RH = NW / 4;                         // row parts (waves per column group)
+    static constexpr int MI = BM / 32, MIW = MI / RH, NJ = 2; // m-blocks per tile / per wave
     static constexpr int CH = ROWB / 16;                      // 16-byte chunks per activation row
     static constexpr int BF = ROWB / 32;                      // weight KB per n-block per step
     static constexpr int RPI = 1024 / ROWB;                   // activation rows per DMA instruction
     static constexpr int AS = FP8 ? (BM + 63) / 64 : 0;       // fp8 row-scale DMA instructions per wave per step
-    static constexpr int BI = NJ * BF;                        // weight DMA instructions per wave per step
+    static constexpr int BI = NJ * BF;                        // weight KB per column group per step
+    static constexpr int BIW = BI / RH;                       // weight DMA instructions per wave per step
     static constexpr int ABYTES = BM * ROWB;
-    static constexpr int BBYTES = NW * BI * 1024;
+    static constexpr int BBYTES = 4 * BI * 1024;
     static constexpr int STAGE = ABYTES + BBYTES + AS * 256;
     static constexpr int EXTRA = FP8 ? NW * NJ * 64 * 4 : 0;  // fp8: weight block scales (K / 128 <= 64)
     static constexpr int FIT = (163840 - EXTRA) / STAGE;
@@ -522,12 +530,13 @@ struct FragCfg {
     static_assert(BM % 32 == 0 && (ROWB == 64 || ROWB == 128), "tile shape");
     static_assert(!FP8 || ROWB == 128, "fp8 steps are one 128-wide scale block");
     static_assert(P >= 1, "ring too shallow");
+    static_assert(BI % RH == 0 && MI % RH == 0, "waves split the tile evenly");
 };
 
 // activation rows a tile with MA active m-blocks loads (a whole number of DMA instructions per wave)
-template <int ROWB, int MA>
+template <int ROWB, int MA, int NW>
 constexpr int loaded_rows() {
-    constexpr int unit = 4 * (1024 / ROWB);
+    constexpr int unit = NW * (1024 / ROWB);
     return ((MA * 32 + unit - 1) / unit) * unit;
 }
 
@@ -545,14 +554,20 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                                           const float* s_bscale) {
     using C = FragCfg<BM, ROWB, FP8>;
     constexpr int NS = C::NS, P = C::P, NJ = C::NJ, CH = C::CH, BF = C::BF, STAGE = C::STAGE;
-    constexpr int AS = C::AS, BI = C::BI, ABYTES = C::ABYTES, BBYTES = C::BBYTES;
-    constexpr int RPI = C::RPI;
+    constexpr int AS = C::AS, BI = C::BI, BIW = C::BIW, ABYTES = C::ABYTES, BBYTES = C::BBYTES;
+    constexpr int RPI = C::RPI, NW = C::NW, MIW = C::MIW;
     // only the rows of the MA active m-blocks are loaded: each wave DMAs an equal share of them
-    constexpr int AI = loaded_rows<ROWB, MA>() / C::NW / RPI;
-    constexpr int PER = AI + AS + BI;
-    static_assert(AI >= 1 && loaded_rows<ROWB, MA>() <= BM, "activation rows must split evenly over the waves");
+    constexpr int AI = loaded_rows<ROWB, MA, NW>() / NW / RPI;
+    constexpr int PER = AI + AS + BIW;
+    // a wave multiplies MW m-blocks of its row part, or none when its part holds no active rows
+    constexpr int MW = MA < MIW ? MA : MIW;
+    static_assert(AI >= 1 && loaded_rows<ROWB, MA, NW>() <= BM, "activation rows must split evenly over the waves");
+    static_assert(C::RH == 1 || MA <= MIW || MA % MIW == 0, "row parts are all active or all idle");
     static_assert(PER * P < 64, "vmcnt budget");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cg = wave & 3, rh = C::RH == 1 ? 0 : wave >> 2;   // column group, row part
+    const bool active = rh * MIW < MA;
+    const int rbase = rh * MIW * 32;                   // first tile row of this wave's part
     const int l32 = lane & 31, hi = lane >> 5;
     const Tile& t = c.t;
     const int KT = c.KT;
@@ -571,9 +586,19 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         for (int i = 0; i < AS; ++i) gs[i] = p.a_scale + (size_t)(t.row0 + min(i * 64 + lane, t.nrows - 1)) * KB;
     }
 
-    f32x16 acc[MA][NJ];
+    // this wave's share of its column group's weight fragments: BIW of the group's NJ * BF per step
+    const uint8_t* gb[BIW];
+    int lb[BIW];
 #pragma unroll
-    for (int i = 0; i < MA; ++i)
+    for (int q = 0; q < BIW; ++q) {
+        const int idx = rh * BIW + q;                  // = j * BF + v
+        gb[q] = (idx < BF ? c.wb[0] : c.wb[1]) + (idx % BF) * 1024;
+        lb[q] = ABYTES + (cg * BI + idx) * 1024;
+    }
+
+    f32x16 acc[MW][NJ];
+#pragma unroll
+    for (int i = 0; i < MW; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -584,10 +609,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
 #pragma unroll
         for (int i = 0; i < AI; ++i) dma16(ga[i] + (size_t)kt * ROWB, st + (wave * AI + i) * 1024);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int v = 0; v < BF; ++v)
-                dma16(c.wb[j] + ((size_t)kt * BF + v) * 1024, st + ABYTES + (wave * BI + j * BF + v) * 1024);
+        for (int q = 0; q < BIW; ++q) dma16(gb[q] + (size_t)kt * BF * 1024, st + lb[q]);
         if constexpr (FP8) {
 #pragma unroll
             for (int i = 0; i < AS; ++i)
@@ -595,30 +617,20 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         }
     };
     auto a_frag = [&](const uint8_t* A, int i, int chunk) -> u32x4 {
-        const int row = i * 32 + l32;
+        const int row = rbase + i * 32 + l32;
         return *reinterpret_cast<const u32x4*>(A + row * ROWB + (aslot<ROWB>(row, chunk) << 4));
     };
     auto b_frag = [&](const uint8_t* B, int j, int v) -> u32x4 {
-        return *reinterpret_cast<const u32x4*>(B + (wave * BI + j * BF + v) * 1024 + lane * 16);
+        return *reinterpret_cast<const u32x4*>(B + (cg * BI + j * BF + v) * 1024 + lane * 16);
     };
+    // fp8 step: per m-block, the two 64-wide halves of the 128-wide K block go through the scaled
+    // MFMA (unit scales) into a fresh partial sum, which is folded into the accumulator with the
+    // row scale times the weight block's scale.
     auto compute = [&](int kt, int buf) {
         const uint8_t* A = smem + buf * STAGE;
         const uint8_t* B = A + ABYTES;
-        if constexpr (!FP8) {
-#pragma unroll
-            for (int s = 0; s < ROWB / 32; ++s) {
-                bf16x8 bf[NJ];
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) bf[j] = __builtin_bit_cast(bf16x8, b_frag(B, j, s));
-#pragma unroll
-                for (int i = 0; i < MA; ++i) {
-                    const bf16x8 af = __builtin_bit_cast(bf16x8, a_frag(A, i, s * 2 + hi));
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[j], acc[i][j], 0, 0, 0);
-                }
-            }
-        } else {
+        if constexpr (FP8) {
+            if (!active) return;
             const float* sa_lds = reinterpret_cast<const float*>(B + BBYTES);
             float sb[NJ];
 #pragma unroll
@@ -633,7 +645,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                                      (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
                 }
 #pragma unroll
-            for (int i = 0; i < MA; ++i) {
+            for (int i = 0; i < MW; ++i) {
                 i32x8 af[2];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
@@ -644,7 +656,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                 float sa[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 v = *reinterpret_cast<const float4*>(sa_lds + i * 32 + q * 8 + hi * 4);
+                    const float4 v = *reinterpret_cast<const float4*>(sa_lds + rbase + i * 32 + q * 8 + hi * 4);
                     sa[4 * q] = v.x;
                     sa[4 * q + 1] = v.y;
                     sa[4 * q + 2] = v.z;
@@ -671,7 +683,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         // run; the last sub-step of a step first crosses the barrier into the next step's slot.
         constexpr int S = ROWB / 32;
         struct Frags {
-            bf16x8 a[MA];
+            bf16x8 a[MW];
             bf16x8 b[NJ];
         };
         Frags F[2];
@@ -681,11 +693,11 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
 #pragma unroll
             for (int j = 0; j < NJ; ++j) f.b[j] = __builtin_bit_cast(bf16x8, b_frag(B, j, sub));
 #pragma unroll
-            for (int i = 0; i < MA; ++i) f.a[i] = __builtin_bit_cast(bf16x8, a_frag(A, i, sub * 2 + hi));
+            for (int i = 0; i < MW; ++i) f.a[i] = __builtin_bit_cast(bf16x8, a_frag(A, i, sub * 2 + hi));
         };
         auto mma = [&](const Frags& f) {
 #pragma unroll
-            for (int i = 0; i < MA; ++i)
+            for (int i = 0; i < MW; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
@@ -713,7 +725,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         // Interleave the next fragments' ds_reads one by one between this sub-step's MFMAs: the LDS
         // counter is 4 bits, so a batch of reads issued ahead of still-pending ones would force a
         // full drain (lgkmcnt(0)) before the first MFMA.
-        constexpr int NL = MA + NJ, NM = MA * NJ, PERL = (NM + NL - 1) / NL;
+        constexpr int NL = MW + NJ, NM = MW * NJ, PERL = (NM + NL - 1) / NL;
         auto interleave = [&]() {
 #pragma unroll
             for (int q = 0; q < NL; ++q) {
@@ -782,66 +794,70 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     }
 
     // ---------------------------------------------------------------- epilogue
-    auto row_of = [&](int i, int r) -> int { return i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3); };
+    auto row_of = [&](int i, int r) -> int { return rbase + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3); };
     if constexpr (KIND == kGemm1) {
-        const int col = t.nt * 128 + wave * 32 + l32;     // A column of this lane
+        const int col = t.nt * 128 + cg * 32 + l32;       // A column of this lane
         if constexpr (!FP8) {
             uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
-            for (int i = 0; i < MA; ++i)
+            for (int i = 0; i < MW; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = row_of(i, r);
                     if (m < t.nrows) out[(size_t)(t.row0 + m) * p.N + col] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
                 }
         } else {
-            // the tile's 128 A columns are exactly one quantisation group: amax over the 4 waves
+            // the tile's 128 A columns are exactly one quantisation group: amax over the 4 column groups
             ordered_barrier();                                   // every wave is done with the ring
-            float* red = reinterpret_cast<float*>(smem);         // [NW][BM]
-            float av[MA][16];
+            float* red = reinterpret_cast<float*>(smem);         // [4][BM]
+            float av[MW][16];
+            if (active) {
 #pragma unroll
-            for (int i = 0; i < MA; ++i)
+                for (int i = 0; i < MW; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    av[i][r] = silu_mul(acc[i][0][r], acc[i][1][r]);
-                    float m = fabsf(av[i][r]);
+                    for (int r = 0; r < 16; ++r) {
+                        av[i][r] = silu_mul(acc[i][0][r], acc[i][1][r]);
+                        float m = fabsf(av[i][r]);
 #pragma unroll
-                    for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
-                    if (l32 == 0) red[wave * BM + row_of(i, r)] = m;
-                }
+                        for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+                        if (l32 == 0) red[cg * BM + row_of(i, r)] = m;
+                    }
+            }
             __syncthreads();
             const int IB = p.N / kFp8Group;
+            if (active) {
 #pragma unroll
-            for (int i = 0; i < MA; ++i)
+                for (int i = 0; i < MW; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = row_of(i, r);
-                    const float amax = fmaxf(fmaxf(red[m], red[BM + m]), fmaxf(red[2 * BM + m], red[3 * BM + m]));
-                    const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
-                    if (m < t.nrows) {
-                        p.out[(size_t)(t.row0 + m) * p.N + col] = f32_to_e4m3(av[i][r] / sc);
-                        if (wave == 0 && l32 == 0) p.out_scale[(size_t)(t.row0 + m) * IB + t.nt] = sc;
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = row_of(i, r);
+                        const float amax = fmaxf(fmaxf(red[m], red[BM + m]), fmaxf(red[2 * BM + m], red[3 * BM + m]));
+                        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+                        if (m < t.nrows) {
+                            p.out[(size_t)(t.row0 + m) * p.N + col] = f32_to_e4m3(av[i][r] / sc);
+                            if (cg == 0 && l32 == 0) p.out_scale[(size_t)(t.row0 + m) * IB + t.nt] = sc;
+                        }
                     }
-                }
+            }
         }
-    } else {
+    } else if (active) {
         uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
-        for (int i = 0; i < MA; ++i)
+        for (int i = 0; i < MW; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = row_of(i, r);
                     if (m < t.nrows)
-                        out[(size_t)(t.row0 + m) * p.N + t.nt * 256 + wave * 64 + j * 32 + l32] = f32_to_bf16(acc[i][j][r]);
+                        out[(size_t)(t.row0 + m) * p.N + t.nt * 256 + cg * 64 + j * 32 + l32] = f32_to_bf16(acc[i][j][r]);
                 }
     }
 }
 
 template <int BM, int KIND, bool FP8>
-__global__ __launch_bounds__(256, 1) void gemm_frag_kernel(GemmParams p) {
-    constexpr int ROWB = (FP8 || BM == 32) ? 128 : 64;
+__global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) void gemm_frag_kernel(GemmParams p) {
+    constexpr int ROWB = rowb_of(BM, FP8);
     using C = FragCfg<BM, ROWB, FP8>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE + C::EXTRA];
     float* s_bscale = reinterpret_cast<float*>(smem + C::NS * C::STAGE);   // fp8 only
@@ -862,7 +878,8 @@ __global__ __launch_bounds__(256, 1) void gemm_frag_kernel(GemmParams p) {
     const size_t nblk_bytes = (size_t)p.K * (FP8 ? 1 : 2) * 32;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        c.nblk[j] = KIND == kGemm1 ? (j == 0 ? 0 : p.I / 32) + c.t.nt * 4 + wave : c.t.nt * 8 + wave * 2 + j;
+        const int cg = wave & 3;
+        c.nblk[j] = KIND == kGemm1 ? (j == 0 ? 0 : p.I / 32) + c.t.nt * 4 + cg : c.t.nt * 8 + cg * 2 + j;
         c.wb[j] = wbase + (size_t)c.nblk[j] * nblk_bytes + lane * 16;
     }
     if constexpr (FP8) {
@@ -880,6 +897,10 @@ __global__ __launch_bounds__(256, 1) void gemm_frag_kernel(GemmParams p) {
     } else if constexpr (C::MI == 2) {
         if (ma <= 1) frag_tile<BM, ROWB, 1, KIND, FP8>(p, c, smem, s_bscale);
         else frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
+    } else if constexpr (C::MI == 4 && C::NW == 8) {
+        // two 64-row parts: one or both active
+        if (ma <= 2) frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
+        else frag_tile<BM, ROWB, 4, KIND, FP8>(p, c, smem, s_bscale);
     } else if constexpr (C::MI == 4) {
         if (ma <= 1) frag_tile<BM, ROWB, 1, KIND, FP8>(p, c, smem, s_bscale);
         else if (ma == 2) frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
@@ -1062,7 +1083,8 @@ void launch_f32(const GemmParams& p, int64_t tiles, hipStream_t st) {
 
 template <int BM, int KIND, bool FP8>
 void launch_dma(const GemmParams& p, int64_t tiles, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_frag_kernel<BM, KIND, FP8>), dim3((unsigned)xcd_grid(tiles)), dim3(256), 0, st, p);
+    constexpr int threads = FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64;
+    hipLaunchKernelGGL((gemm_frag_kernel<BM, KIND, FP8>), dim3((unsigned)xcd_grid(tiles)), dim3(threads), 0, st, p);
 }
 
 template <int BM>
