@@ -502,14 +502,16 @@ struct TileCtx {
 // ROWB: bytes of one activation row per K step (64 or 128).  Weight fragments are 1 KB per 16 bf16
 // (or per 64 fp8 / 2 halves) K columns, so a step moves ROWB / 32 fragment-KB per n-block.
 //
-// Waves: four column groups of 64 output columns each.  bf16 tiles have one wave per column group
-// holding all BM rows.  fp8 tiles of 128 rows have two waves per column group, one per 64-row part
-// (two waves per SIMD), so that one wave's fp32 scale fold runs while the other's MFMAs do.
+// Waves: four column groups of 64 output columns each.  Tiles up to 128 rows (bf16) have one wave
+// per column group holding all BM rows.  bf16 tiles of 256 rows and fp8 tiles of 128 rows have two
+// waves per column group, one per half of the rows (two waves per SIMD): the SIMD switches to the
+// other wave while one waits on LDS or the barrier, and for fp8 one wave's fp32 scale fold runs
+// while the other's MFMAs do.
 constexpr int rowb_of(int BM, bool FP8) { return (FP8 || BM == 32) ? 128 : 64; }
 
 template <int BM, int ROWB, bool FP8>
 struct FragCfg {
-    static constexpr int NW = (FP8 && BM >= 128) ? 8 : 4;    // waves
+    static constexpr int NW = (FP8 ? BM >= 128 : BM >= 256) ? 8 : 4;   // waves
     static constexpr int RH = NW / 4;                         // row parts (waves per column group)
     static constexpr int MI = BM / 32, MIW = MI / RH, NJ = 2; // m-blocks per tile / per wave
     static constexpr int CH = ROWB / 16;                      // 16-byte chunks per activation row
@@ -692,6 +694,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         };
         Frags F[2];
         auto load = [&](Frags& f, int buf, int sub) {
+            if (!active) return;
             const uint8_t* A = smem + buf * STAGE;
             const uint8_t* B = A + ABYTES;
 #pragma unroll
@@ -700,6 +703,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
             for (int i = 0; i < MW; ++i) f.a[i] = __builtin_bit_cast(bf16x8, a_frag(A, i, sub * 2 + hi));
         };
         auto mma = [&](const Frags& f) {
+            if (!active) return;
 #pragma unroll
             for (int i = 0; i < MW; ++i)
 #pragma unroll
@@ -894,7 +898,7 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
         }
         __syncthreads();
     }
-    // active 32-row m-blocks; 256-row tiles round up to even counts to bound the variants
+    // active 32-row m-blocks (8-wave tiles: whole row parts)
     const int ma = (c.t.nrows + 31) / 32;
     if constexpr (C::MI == 1) {
         frag_tile<BM, ROWB, 1, KIND, FP8>(p, c, smem, s_bscale);
@@ -910,14 +914,10 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
         else if (ma == 2) frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
         else if (ma == 3) frag_tile<BM, ROWB, 3, KIND, FP8>(p, c, smem, s_bscale);
         else frag_tile<BM, ROWB, 4, KIND, FP8>(p, c, smem, s_bscale);
-    } else if constexpr (C::NW == 8) {
+    } else {
+        static_assert(C::NW == 8, "256-row tiles run on 8 waves");
         // two 128-row parts: one or both active
         if (ma <= 4) frag_tile<BM, ROWB, 4, KIND, FP8>(p, c, smem, s_bscale);
-        else frag_tile<BM, ROWB, 8, KIND, FP8>(p, c, smem, s_bscale);
-    } else {
-        if (ma <= 2) frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
-        else if (ma <= 4) frag_tile<BM, ROWB, 4, KIND, FP8>(p, c, smem, s_bscale);
-        else if (ma <= 6) frag_tile<BM, ROWB, 6, KIND, FP8>(p, c, smem, s_bscale);
         else frag_tile<BM, ROWB, 8, KIND, FP8>(p, c, smem, s_bscale);
     }
 }
