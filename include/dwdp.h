@@ -131,12 +131,21 @@ int dwdp_route_topk(const void* x, const void* w_router, int in_dtype, const flo
  *   codes (uint8) and x_perm_scale [rows, H/128] the scales.
  *   Outputs: x_perm [rows,H], offsets [E+shared+1], perm_src [rows] (source token
  *   of each row), inv_perm [T,k] (row of each (t,j)).
+ *   x_perm == NULL computes only offsets, perm_src and inv_perm (x, x_perm_scale
+ *   are then not read): the caller feeds the tokens to
+ *   dwdp_moe_grouped_ffn_tokens, which gathers the rows itself.
  *   ws: dwdp_workspace_bytes(DWDP_OP_PERMUTE, ...) bytes of device scratch. */
 int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, int shared,
                  const void* x, int x_dtype, int act_dtype, int H,
                  void* x_perm, float* x_perm_scale,
                  int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* Per-token fp8 quantisation, exactly as dwdp_permute quantises a row:
+ *   x [T,H] bf16 (16-byte aligned), H % 128 == 0.  q [T,H] E4M3 codes, q_scale
+ *   [T,H/128] fp32: per 128-column group scale = amax/448 (1 when amax is 0),
+ *   code = E4M3(value/scale), nearest even, saturating.  T == 0 is a no-op. */
+int dwdp_quantize_tokens_fp8(const void* x, int64_t T, int H, void* q, float* q_scale, void* stream);
 
 /* Grouped SwiGLU FFN, reading each group's weights through `table` (device
  * array of n_groups entries) -- no merge of the split buffers (paper summary §4.2).
@@ -168,6 +177,18 @@ int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups, const int3
 int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,
                                const void* x_perm, const float* x_perm_scale, int64_t rows, int H, int I,
                                int w_dtype, void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* The grouped FFN reading token rows instead of permuted rows: GEMM1's row r is
+ * x[perm_src[r]] (out-of-range indices clamp to [0, T)), which spares the row
+ * gather of dwdp_permute and its x_perm round trip through HBM.  x [T,H] holds the
+ * tokens (F32 / BF16 as w_dtype; for FP8 the codes of dwdp_quantize_tokens_fp8
+ * with x_scale [T,H/128]).  Everything else -- stage, table, offsets, rows,
+ * workspace, outputs -- is as in dwdp_moe_grouped_ffn_stage, and the results
+ * are bitwise those of the x_perm path. */
+int dwdp_moe_grouped_ffn_tokens(int stage, const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,
+                                const int32_t* perm_src, const void* x, const float* x_scale, int64_t T,
+                                int64_t rows, int H, int I, int w_dtype, void* y_perm, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /* Combine: y[t] = sum_{j<k} topk_w[t,j] * y_perm[inv_perm[t,j]] (+ y_perm[T*k + t]
  * when shared), summed in fp32 in slot order then the shared row, rounded once

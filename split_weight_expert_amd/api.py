@@ -80,6 +80,22 @@ def moe_grouped_ffn_stage(stage, table, n_groups, offsets, x_perm, x_perm_scale,
                                                       _stream(stream)))
 
 
+def moe_grouped_ffn_tokens(stage, table, n_groups, offsets, perm_src, x, x_scale, H, I, w_dtype, y_perm, ws,
+                           stream=None):
+    """Grouped FFN whose GEMM1 reads token rows x[perm_src[r]] (no x_perm)."""
+    rows = perm_src.shape[0]
+    T = x.shape[0]
+    _lib.check(_lib.load().dwdp_moe_grouped_ffn_tokens(stage, _ptr(table), n_groups, _ptr(offsets), _ptr(perm_src),
+                                                       _ptr(x), _ptr(x_scale), T, rows, H, I, w_dtype, _ptr(y_perm),
+                                                       _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                                       _stream(stream)))
+
+
+def quantize_tokens_fp8(x, q, q_scale, stream=None):
+    T, H = x.shape
+    _lib.check(_lib.load().dwdp_quantize_tokens_fp8(_ptr(x), T, H, _ptr(q), _ptr(q_scale), _stream(stream)))
+
+
 def combine(y_perm, inv_perm, topk_w, shared, y, stream=None):
     T, k = inv_perm.shape
     H = y.shape[1]

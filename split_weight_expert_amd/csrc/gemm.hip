@@ -48,7 +48,9 @@ struct MTile {
 
 struct GemmParams {
     const uint8_t* a;               // activation rows [rows, K]
-    const float* a_scale;           // fp8: [rows, K/128]
+    const float* a_scale;           // fp8: [a_nrows, K/128]
+    const int32_t* a_rows;          // GEMM1: activation row of permuted row r (token mode), or null
+    int64_t a_nrows;                // rows of a
     const dwdp_expert_ptrs* table;  // GEMM1 / GEMM2: per-group weights
     const uint8_t* b_single;        // router: weight [N, K]
     const float* bias;              // router: bias [N] or null
@@ -71,6 +73,13 @@ struct Tile {
     int64_t row0;
     int nrows;
 };
+
+// Row of the activation matrix that holds permuted row prow: itself, or its token (clamped).
+__device__ __forceinline__ int64_t act_row(const GemmParams& p, int64_t prow) {
+    if (p.a_rows == nullptr) return prow;
+    const int64_t r = p.a_rows[prow];
+    return r < 0 ? 0 : (r >= p.a_nrows ? p.a_nrows - 1 : r);
+}
 
 // Tiles reach the XCDs in clusters: workgroup b runs on XCD b % 8, and XCD x takes clusters x, x+8,
 // x+16, ... of kCluster consecutive tiles, in order.  Consecutive tiles share operands (below), so a
@@ -580,7 +589,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
         const int r = (wave * AI + i) * RPI + lane / CH;
-        ga[i] = p.a + (size_t)(t.row0 + min(r, t.nrows - 1)) * lda + aslot<ROWB>(r, lane % CH) * 16;
+        ga[i] = p.a + (size_t)act_row(p, t.row0 + min(r, t.nrows - 1)) * lda + aslot<ROWB>(r, lane % CH) * 16;
     }
     // fp8: each wave loads one 256-byte slice (64 rows) of the step's row scales; slices repeat
     // over the waves, so every wave issues the same count
@@ -588,7 +597,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     [[maybe_unused]] int ls = 0;
     if constexpr (FP8) {
         const int KB = p.K / kFp8Group, sl = wave % C::SL;
-        gs = p.a_scale + (size_t)(t.row0 + min(sl * 64 + lane, t.nrows - 1)) * KB;
+        gs = p.a_scale + (size_t)act_row(p, t.row0 + min(sl * 64 + lane, t.nrows - 1)) * KB;
         ls = ABYTES + BBYTES + sl * 256;
     }
 
@@ -984,7 +993,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
         for (int i = 0; i < 4; ++i) {
             const int lin = tid + i * 256, r = lin >> 4, kk = lin & 15;
             const int rr = min(r, t.nrows - 1);
-            sA[kk][r] = A[(size_t)(t.row0 + rr) * p.K + k0 + kk];
+            sA[kk][r] = A[(size_t)act_row(p, t.row0 + rr) * p.K + k0 + kk];
             sB[kk][r] = W[(size_t)w_row(r) * p.K + k0 + kk];
         }
         __syncthreads();
@@ -1151,10 +1160,13 @@ int router_gemm(const void* x, const void* w, int dtype, const float* bias, int6
 
 using namespace dwdp;
 
-extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* table, int n_groups,
-                                          const int32_t* offsets, const void* x_perm, const float* x_perm_scale,
-                                          int64_t rows, int H, int I, int w_dtype, void* y_perm, void* ws,
-                                          size_t ws_bytes, void* stream) {
+namespace {
+
+// The grouped FFN.  a_rows == nullptr: GEMM1's activation row r is x row r (x holds the permuted
+// rows); otherwise it is x row a_rows[r] (x holds the x_rows token rows).
+int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets, const int32_t* a_rows,
+                const void* x, const float* x_scale, int64_t x_rows, int64_t rows, int H, int I, int w_dtype,
+                void* y_perm, void* ws, size_t ws_bytes, void* stream) {
     clear_error();
     DWDP_REQUIRE(stage >= 0 && stage <= 2, "stage must be 0, 1 or 2");
     DWDP_REQUIRE(w_dtype == DWDP_F32 || w_dtype == DWDP_BF16 || w_dtype == DWDP_FP8_E4M3, "unknown w_dtype");
@@ -1168,10 +1180,11 @@ extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* tab
         if (w_dtype == DWDP_FP8_E4M3) DWDP_REQUIRE(H <= 8192 && I <= 8192, "fp8 path needs H, I <= 8192");
     }
     if (rows == 0) return DWDP_OK;
-    DWDP_REQUIRE(table && offsets && x_perm && ws && (y_perm || stage == 1), "null pointer argument");
-    DWDP_REQUIRE(aligned16(table) && aligned16(x_perm) && aligned16(y_perm) && aligned16(ws),
+    DWDP_REQUIRE(table && offsets && x && ws && (y_perm || stage == 1), "null pointer argument");
+    DWDP_REQUIRE(aligned16(table) && aligned16(x) && aligned16(y_perm) && aligned16(ws),
                  "pointers must be 16-byte aligned");
-    if (w_dtype == DWDP_FP8_E4M3) DWDP_REQUIRE(x_perm_scale != nullptr, "fp8 needs x_perm_scale");
+    DWDP_REQUIRE(x_rows >= 1 && x_rows < ((int64_t)1 << 31), "x_rows out of range");
+    if (w_dtype == DWDP_FP8_E4M3) DWDP_REQUIRE(x_scale != nullptr, "fp8 needs the activation scales");
     FfnWs L = ffn_ws_layout(rows, n_groups, I, w_dtype);
     if (ws_bytes < L.total)
         return fail(DWDP_ERR_WORKSPACE, "dwdp_moe_grouped_ffn: workspace too small (need " + std::to_string(L.total) + ")");
@@ -1181,8 +1194,10 @@ extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* tab
     const int64_t maxm = (rows + bm - 1) / bm + n_groups;
 
     GemmParams p1{};
-    p1.a = static_cast<const uint8_t*>(x_perm);
-    p1.a_scale = x_perm_scale;
+    p1.a = static_cast<const uint8_t*>(x);
+    p1.a_scale = x_scale;
+    p1.a_rows = a_rows;
+    p1.a_nrows = x_rows;
     p1.table = table;
     p1.offsets = offsets;
     p1.mprefix = reinterpret_cast<int32_t*>(base + L.pre);
@@ -1198,6 +1213,8 @@ extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* tab
     GemmParams p2 = p1;
     p2.a = base + L.a;
     p2.a_scale = reinterpret_cast<const float*>(base + L.a_scale);
+    p2.a_rows = nullptr;
+    p2.a_nrows = rows;
     p2.N = H;
     p2.K = I;
     p2.NT = w_dtype == DWDP_F32 ? H / kBnF32 : H / kBnDma;
@@ -1220,6 +1237,27 @@ extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* tab
     }
     DWDP_LAUNCHED();
     return DWDP_OK;
+}
+
+}  // namespace
+
+extern "C" int dwdp_moe_grouped_ffn_stage(int stage, const dwdp_expert_ptrs* table, int n_groups,
+                                          const int32_t* offsets, const void* x_perm, const float* x_perm_scale,
+                                          int64_t rows, int H, int I, int w_dtype, void* y_perm, void* ws,
+                                          size_t ws_bytes, void* stream) {
+    return grouped_ffn(stage, table, n_groups, offsets, nullptr, x_perm, x_perm_scale, rows > 0 ? rows : 1, rows, H, I,
+                       w_dtype, y_perm, ws, ws_bytes, stream);
+}
+
+extern "C" int dwdp_moe_grouped_ffn_tokens(int stage, const dwdp_expert_ptrs* table, int n_groups,
+                                           const int32_t* offsets, const int32_t* perm_src, const void* x,
+                                           const float* x_scale, int64_t T, int64_t rows, int H, int I, int w_dtype,
+                                           void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    DWDP_REQUIRE(rows == 0 || perm_src != nullptr, "perm_src is NULL");
+    DWDP_REQUIRE(rows == 0 || T >= 1, "T must be positive");
+    return grouped_ffn(stage, table, n_groups, offsets, perm_src, x, x_scale, T, rows, H, I, w_dtype, y_perm, ws,
+                       ws_bytes, stream);
 }
 
 extern "C" int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,

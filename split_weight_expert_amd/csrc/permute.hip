@@ -164,7 +164,14 @@ __global__ __launch_bounds__(256) void gather_copy_kernel(const uint8_t* __restr
     for (int64_t i = threadIdx.x; i < nvec; i += 256) out[i] = ok ? in[i] : uint4{0, 0, 0, 0};
 }
 
-// fp8 gather: 16 lanes per 128-column group, 8 bf16 values (16 bytes) per lane.
+// Shared-expert rows of perm_src (token t at row R + t) when no rows are gathered.
+__global__ __launch_bounds__(256) void shared_rows_kernel(int32_t* __restrict__ perm_src, int64_t R, int64_t T) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t < T) perm_src[R + t] = (int32_t)t;
+}
+
+// fp8 gather: 16 lanes per 128-column group, 8 bf16 values (16 bytes) per lane.  perm_src == NULL
+// quantises x row by row (output row r = token r).
 __global__ __launch_bounds__(256) void gather_fp8_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t R, int H,
                                                          int32_t* __restrict__ perm_src, uint8_t* __restrict__ q,
                                                          float* __restrict__ qs) {
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(256) void gather_fp8_kernel(const uint16_t* __restr
         src = perm_src[r];
     } else {
         src = r - R;
-        if (threadIdx.x == 0) perm_src[r] = (int32_t)src;
+        if (perm_src != nullptr && threadIdx.x == 0) perm_src[r] = (int32_t)src;
     }
     const bool ok = src >= 0 && src < T;
     const int G = H / kFp8Group;
@@ -236,10 +243,14 @@ extern "C" int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, in
     DWDP_REQUIRE(offsets != nullptr, "offsets is NULL");
     const size_t need = permute_ws_bytes(T, k, E);
     if (T == 0) return DWDP_OK;
-    DWDP_REQUIRE(topk_idx && x && x_perm && perm_src && inv_perm && ws, "null pointer argument");
-    DWDP_REQUIRE(aligned16(topk_idx) && aligned16(x) && aligned16(x_perm) && aligned16(ws),
-                 "topk_idx, x, x_perm and ws must be 16-byte aligned");
-    if (act_dtype == DWDP_FP8_E4M3) DWDP_REQUIRE(x_perm_scale != nullptr, "fp8 needs x_perm_scale");
+    DWDP_REQUIRE(topk_idx && perm_src && inv_perm && ws, "null pointer argument");
+    const bool gather = x_perm != nullptr;
+    if (gather) {
+        DWDP_REQUIRE(x != nullptr, "x is NULL");
+        DWDP_REQUIRE(aligned16(x) && aligned16(x_perm), "x and x_perm must be 16-byte aligned");
+        if (act_dtype == DWDP_FP8_E4M3) DWDP_REQUIRE(x_perm_scale != nullptr, "fp8 needs x_perm_scale");
+    }
+    DWDP_REQUIRE(aligned16(topk_idx) && aligned16(ws), "topk_idx and ws must be 16-byte aligned");
     if (ws_bytes < need) return fail(DWDP_ERR_WORKSPACE, "dwdp_permute: workspace too small");
     hipStream_t st = as_stream(stream);
     const int64_t N = T * k, R = N, rows = R + shared * T;
@@ -249,7 +260,9 @@ extern "C" int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, in
     hipLaunchKernelGGL(count_kernel, dim3(E), dim3(1024), 0, st, topk_idx, N, seg, wave_counts);
     hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, wave_counts, E, shared, T, R, offsets, wave_base);
     hipLaunchKernelGGL(scatter_kernel, dim3(E), dim3(1024), 0, st, topk_idx, N, k, E, seg, wave_base, perm_src, inv_perm);
-    if (act_dtype == DWDP_FP8_E4M3) {
+    if (!gather) {
+        if (shared) hipLaunchKernelGGL(shared_rows_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, perm_src, R, T);
+    } else if (act_dtype == DWDP_FP8_E4M3) {
         hipLaunchKernelGGL(gather_fp8_kernel, dim3((unsigned)rows), dim3(256), 0, st,
                            static_cast<const uint16_t*>(x), T, R, H, perm_src, static_cast<uint8_t*>(x_perm),
                            x_perm_scale);
@@ -257,6 +270,20 @@ extern "C" int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, in
         hipLaunchKernelGGL(gather_copy_kernel, dim3((unsigned)rows), dim3(256), 0, st, static_cast<const uint8_t*>(x), T,
                            R, (int64_t)H * (int64_t)elem_bytes(x_dtype), perm_src, static_cast<uint8_t*>(x_perm));
     }
+    DWDP_LAUNCHED();
+    return DWDP_OK;
+}
+
+extern "C" int dwdp_quantize_tokens_fp8(const void* x, int64_t T, int H, void* q, float* q_scale, void* stream) {
+    clear_error();
+    DWDP_REQUIRE(T >= 0 && T < ((int64_t)1 << 31), "T out of range");
+    DWDP_REQUIRE(H > 0 && H % kFp8Group == 0, "H must be a positive multiple of 128");
+    if (T == 0) return DWDP_OK;
+    DWDP_REQUIRE(x && q && q_scale, "null pointer argument");
+    DWDP_REQUIRE(aligned16(x) && aligned16(q), "x and q must be 16-byte aligned");
+    hipLaunchKernelGGL(gather_fp8_kernel, dim3((unsigned)T), dim3(256), 0, as_stream(stream),
+                       static_cast<const uint16_t*>(x), T, (int64_t)0, H, static_cast<int32_t*>(nullptr),
+                       static_cast<uint8_t*>(q), q_scale);
     DWDP_LAUNCHED();
     return DWDP_OK;
 }

@@ -5,7 +5,10 @@ resident partition and a double-buffered prefetch area (DWDP paper summary,
 §2) -- and builds the per-group pointer table that the grouped GEMM reads
 instead of a merged copy (§4.2).  MoEBlock owns the activation buffers and
 workspaces for a token count and runs route -> permute -> grouped FFN ->
-combine on one stream.  Nothing here computes: every step is a libdwdp call.
+combine on one stream.  By default GEMM1 reads the token rows through the
+permutation (dwdp_moe_grouped_ffn_tokens) and no x_perm is materialised;
+gather=True runs the permute's row gather and the x_perm path instead.
+Nothing here computes: every step is a libdwdp call.
 """
 from __future__ import annotations
 
@@ -102,8 +105,10 @@ class BlockBuffers:
     logits: torch.Tensor
     idx: torch.Tensor
     w: torch.Tensor
-    x_perm: torch.Tensor
-    x_perm_scale: torch.Tensor | None
+    x_perm: torch.Tensor | None          # gather mode: permuted rows (fp8: codes)
+    x_perm_scale: torch.Tensor | None    # gather mode, fp8
+    x_q: torch.Tensor | None             # token mode, fp8: per-token codes [T, H]
+    x_q_scale: torch.Tensor | None       # token mode, fp8: [T, H/128]
     offsets: torch.Tensor
     perm_src: torch.Tensor
     inv_perm: torch.Tensor
@@ -111,15 +116,17 @@ class BlockBuffers:
     y: torch.Tensor
     ws_perm: torch.Tensor
     ws_ffn: torch.Tensor
+    x_tokens: torch.Tensor | None = None  # token mode: the rows GEMM1 reads (x, or x_q for fp8)
 
 
 class MoEBlock:
     """Route -> permute -> grouped SwiGLU FFN -> combine for one layer shape."""
 
-    def __init__(self, H: int, I: int, E: int, k: int, shared: int, dtype: str, device="cuda"):
+    def __init__(self, H: int, I: int, E: int, k: int, shared: int, dtype: str, device="cuda", gather: bool = False):
         self.H, self.I, self.E, self.k, self.shared = H, I, E, k, shared
         self.w_dtype = DTYPES[dtype]
         self.device = device
+        self.gather = gather
         self._bufs: dict[int, BlockBuffers] = {}
 
     def buffers(self, T: int) -> BlockBuffers:
@@ -129,15 +136,18 @@ class MoEBlock:
         rows = T * k + S * T
         adt = act_dtype(self.w_dtype)
         xp_dt = torch.uint8 if self.w_dtype == FP8_E4M3 else adt
+        fp8 = self.w_dtype == FP8_E4M3
+        g = self.gather
         ws_p = api.workspace_bytes(api.OP_PERMUTE, T, k, E, H, I, self.w_dtype, S)
         ws_f = api.workspace_bytes(api.OP_GROUPED_FFN, T, k, E, H, I, self.w_dtype, S)
         b = BlockBuffers(
             logits=torch.empty(T, E, dtype=torch.float32, device=dev),
             idx=torch.empty(T, k, dtype=torch.int32, device=dev),
             w=torch.empty(T, k, dtype=torch.float32, device=dev),
-            x_perm=torch.empty(rows, H, dtype=xp_dt, device=dev),
-            x_perm_scale=(torch.empty(rows, H // 128, dtype=torch.float32, device=dev)
-                          if self.w_dtype == FP8_E4M3 else None),
+            x_perm=torch.empty(rows, H, dtype=xp_dt, device=dev) if g else None,
+            x_perm_scale=torch.empty(rows, H // 128, dtype=torch.float32, device=dev) if g and fp8 else None,
+            x_q=torch.empty(T, H, dtype=torch.uint8, device=dev) if fp8 and not g else None,
+            x_q_scale=torch.empty(T, H // 128, dtype=torch.float32, device=dev) if fp8 and not g else None,
             offsets=torch.empty(E + S + 1, dtype=torch.int32, device=dev),
             perm_src=torch.empty(rows, dtype=torch.int32, device=dev),
             inv_perm=torch.empty(T, k, dtype=torch.int32, device=dev),
@@ -153,16 +163,27 @@ class MoEBlock:
         api.route_topk(x, w_router, bias, self.k, b.logits, b.idx, b.w, stream)
 
     def permute(self, x, b: BlockBuffers, stream=None):
-        api.permute(b.idx, self.E, self.shared, x, self.w_dtype if self.w_dtype == FP8_E4M3 else api.dtype_code(x),
+        """Expert permutation; gather mode also writes x_perm, token mode quantises the tokens for fp8."""
+        fp8 = self.w_dtype == FP8_E4M3
+        api.permute(b.idx, self.E, self.shared, x, self.w_dtype if fp8 else api.dtype_code(x),
                     b.x_perm, b.x_perm_scale, b.offsets, b.perm_src, b.inv_perm, b.ws_perm, stream)
+        if not self.gather:
+            if fp8:
+                api.quantize_tokens_fp8(x, b.x_q, b.x_q_scale, stream)
+                b.x_tokens = b.x_q
+            else:
+                b.x_tokens = x
 
     def ffn(self, table, b: BlockBuffers, stream=None):
-        api.moe_grouped_ffn(table, self.E + self.shared, b.offsets, b.x_perm, b.x_perm_scale, self.H, self.I,
-                            self.w_dtype, b.y_perm, b.ws_ffn, stream)
+        self.ffn_stage(0, table, b, stream)
 
     def ffn_stage(self, stage: int, table, b: BlockBuffers, stream=None):
-        api.moe_grouped_ffn_stage(stage, table, self.E + self.shared, b.offsets, b.x_perm, b.x_perm_scale, self.H,
-                                  self.I, self.w_dtype, b.y_perm, b.ws_ffn, stream)
+        if self.gather:
+            api.moe_grouped_ffn_stage(stage, table, self.E + self.shared, b.offsets, b.x_perm, b.x_perm_scale,
+                                      self.H, self.I, self.w_dtype, b.y_perm, b.ws_ffn, stream)
+        else:
+            api.moe_grouped_ffn_tokens(stage, table, self.E + self.shared, b.offsets, b.perm_src, b.x_tokens,
+                                       b.x_q_scale, self.H, self.I, self.w_dtype, b.y_perm, b.ws_ffn, stream)
 
     def combine(self, b: BlockBuffers, stream=None):
         api.combine(b.y_perm, b.inv_perm, b.w, self.shared, b.y, stream)

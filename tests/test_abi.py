@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lib_mod.SIGNATURES), "binding signatures and header disagree"
@@ -75,7 +75,8 @@ def test_permute_rejects_bad_arguments(lib):
     expect(E_, call(ad=2, xd=0), lib, "act_dtype")
     expect(E_, call(ad=2, xs=None), lib, "x_perm_scale")
     expect(E_, call(ad=2, H=200, xs=FAKE), lib, "H % 128")
-    expect(E_, call(xp=None), lib, "null")
+    expect(E_, call(ps=None), lib, "null")
+    expect(E_, call(xp=FAKE, x=None), lib, "x is NULL")
     expect(lib_mod.DWDP_ERR_WORKSPACE, call(wsb=16), lib, "workspace")
 
 
@@ -84,11 +85,31 @@ def test_grouped_ffn_rejects_bad_arguments(lib):
     E_ = lib_mod.DWDP_ERR_INVALID_ARG
     expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7168, 2048, 5, FAKE, FAKE, 1 << 30, None), lib, "w_dtype")
     expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7040, 2048, 1, FAKE, FAKE, 1 << 30, None), lib, "H % 256")
-    expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7168, 2048, 2, FAKE, FAKE, 1 << 30, None), lib, "x_perm_scale")
+    expect(E_, f(FAKE, 9, FAKE, FAKE, None, 128, 7168, 2048, 2, FAKE, FAKE, 1 << 30, None), lib, "activation scales")
     expect(E_, f(FAKE, 9, FAKE, ODD, None, 128, 7168, 2048, 1, FAKE, FAKE, 1 << 30, None), lib, "aligned")
     expect(lib_mod.DWDP_ERR_WORKSPACE, f(FAKE, 9, FAKE, FAKE, None, 128, 7168, 2048, 1, FAKE, FAKE, 64, None),
            lib, "workspace")
     assert f(None, 9, None, None, None, 0, 7168, 2048, 1, None, None, 0, None) == 0   # rows = 0
+
+
+def test_token_rows_ffn_and_token_quantiser_reject_bad_arguments(lib):
+    f = lib.dwdp_moe_grouped_ffn_tokens
+    E_ = lib_mod.DWDP_ERR_INVALID_ARG
+    # stage, table, n_groups, offsets, perm_src, x, x_scale, T, rows, H, I, w_dtype, y_perm, ws, ws_bytes, stream
+    expect(E_, f(0, FAKE, 9, FAKE, None, FAKE, None, 16, 128, 7168, 2048, 1, FAKE, FAKE, 1 << 30, None), lib,
+           "perm_src")
+    expect(E_, f(0, FAKE, 9, FAKE, FAKE, FAKE, None, 0, 128, 7168, 2048, 1, FAKE, FAKE, 1 << 30, None), lib, "T must")
+    expect(E_, f(3, FAKE, 9, FAKE, FAKE, FAKE, None, 16, 128, 7168, 2048, 1, FAKE, FAKE, 1 << 30, None), lib, "stage")
+    expect(E_, f(0, FAKE, 9, FAKE, FAKE, FAKE, None, 16, 128, 7168, 2048, 2, FAKE, FAKE, 1 << 30, None), lib,
+           "activation scales")
+    expect(lib_mod.DWDP_ERR_WORKSPACE, f(0, FAKE, 9, FAKE, FAKE, FAKE, None, 16, 128, 7168, 2048, 1, FAKE, FAKE, 64,
+                                         None), lib, "workspace")
+    assert f(0, None, 9, None, None, None, None, 0, 0, 7168, 2048, 1, None, None, 0, None) == 0   # rows = 0
+    q = lib.dwdp_quantize_tokens_fp8
+    expect(E_, q(FAKE, 4, 100, FAKE, FAKE, None), lib, "multiple of 128")
+    expect(E_, q(ODD, 4, 128, FAKE, FAKE, None), lib, "aligned")
+    expect(E_, q(FAKE, 4, 128, FAKE, None, None), lib, "null")
+    assert q(None, 0, 128, None, None, None) == 0
 
 
 def test_combine_and_prefetch_reject_bad_arguments(lib):

@@ -9,8 +9,9 @@ permute -> GEMM1+SwiGLU -> GEMM2 -> combine exactly as bench.py does.  Then:
   top-k of those same logits (bit-exact), and its gate weights against the
   oracle's softmax over them;
 * permutation in full: offsets, perm_src and inv_perm bit-exact against the
-  oracle's stable permutation of the GPU's indices, and sampled x_perm rows
-  bit-exact (for fp8: the codes and scales of the oracle's group quantiser);
+  oracle's stable permutation of the GPU's indices (GEMM1 reads the token
+  rows through perm_src; for fp8, sampled tokens' codes and scales are
+  bit-exact against the oracle's group quantiser);
 * expert outputs y_perm on sampled rows (first, last and evenly spaced) of
   the largest group, the smallest non-empty group and the shared expert's
   group, against the oracle's expert FFN of those rows;
@@ -94,16 +95,14 @@ def test_full_size_block(name, n_tokens):
     np.testing.assert_array_equal(b.perm_src.cpu().numpy(), perm_src)
     np.testing.assert_array_equal(b.inv_perm.cpu().numpy(), inv_perm)
     gc = np.diff(offsets)                                   # rows per group, the shared group included
-    rows = np.unique(np.concatenate([offsets[:-1][gc > 0], offsets[1:][gc > 0] - 1,
-                                     np.linspace(0, len(perm_src) - 1, 64).astype(int)]))
-    xp = b.x_perm[torch.from_numpy(rows).cuda()].cpu()
     if cfg.dtype == "fp8":
-        q, s = omoe.quantize_groups(x[perm_src[rows]].astype(np.float32))
-        np.testing.assert_array_equal(xp.numpy(), q)
-        np.testing.assert_array_equal(b.x_perm_scale[torch.from_numpy(rows).cuda()].cpu().numpy(), s)
-    else:
-        np.testing.assert_array_equal(xp.view(torch.int16).numpy(), torch.from_numpy(x[perm_src[rows]]).to(
-            torch.bfloat16).view(torch.int16).numpy())
+        # the tokens GEMM1 reads: per-token codes and scales, bit-exact (sampled tokens)
+        toks_q = np.unique(np.concatenate([[0, cfg.T - 1], perm_src[offsets[:-1][gc > 0]],
+                                           np.linspace(0, cfg.T - 1, 64).astype(int)]))
+        sel = torch.from_numpy(toks_q).cuda()
+        q, s = omoe.quantize_groups(x[toks_q].astype(np.float32))
+        np.testing.assert_array_equal(b.x_q[sel].cpu().numpy(), q)
+        np.testing.assert_array_equal(b.x_q_scale[sel].cpu().numpy(), s)
 
     # ---- expert rows of sampled groups
     G = cfg.E + cfg.shared

@@ -454,3 +454,78 @@ def test_pack_weights_matches_the_documented_layout(dt):
         exp = np.stack([w[rows, cols + e] for e in range(16)], axis=1)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(got, exp)
+
+
+# --------------------------------------------------------------------------------------- token-row GEMM1
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "fp8"])
+def test_token_rows_equal_permuted_rows(dt):
+    """GEMM1 reading token rows through perm_src gives bitwise the x_perm path's A, y_perm and y."""
+    from split_weight_expert_amd import MoEBlock, api
+    name, kw = FFN_CASES[dt]
+    cfg = shrink(synth.get_config(name), **kw)
+    h = HostLayer(cfg, bias=skew_bias(cfg.E))
+    pl, slots = placement_split(cfg)
+    store, table, x, wr, b = upload_layer(h, pl, slots)
+    out = {}
+    for gather in (True, False):
+        blk = MoEBlock(cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, cfg.dtype, DEV, gather=gather)
+        bb = blk.buffers(cfg.T)
+        blk.route(x, wr, b, bb)
+        blk.permute(x, bb)
+        if gather:
+            # the plain entry point (both stages in one call)
+            api.moe_grouped_ffn(table, cfg.E + cfg.shared, bb.offsets, bb.x_perm, bb.x_perm_scale, cfg.H, cfg.I,
+                                blk.w_dtype, bb.y_perm, bb.ws_ffn)
+        else:
+            assert bb.x_perm is None
+            blk.ffn(table, bb)
+        blk.combine(bb)
+        torch.cuda.synchronize()
+        ea = 4 if dt == "f32" else 2 if dt == "bf16" else 1
+        out[gather] = dict(perm_src=bb.perm_src.clone(), offsets=bb.offsets.clone(), y_perm=bb.y_perm.clone(),
+                           y=bb.y.clone(), A=bb.ws_ffn[:cfg.rows * cfg.I * ea].clone())
+    for key in out[True]:
+        assert torch.equal(out[True][key], out[False][key]), key
+
+
+def test_token_quantiser_is_bit_exact():
+    from split_weight_expert_amd import api
+    cfg = shrink(synth.get_config("prefill16k_fp8"), T=300, H=1024)
+    x = synth.tokens(cfg)
+    x[5] = 0.0                                    # an all-zero token: scale 1
+    xt = torch.from_numpy(x).to(DEV, torch.bfloat16)
+    q = torch.empty(cfg.T, cfg.H, dtype=torch.uint8, device=DEV)
+    s = torch.empty(cfg.T, cfg.H // 128, dtype=torch.float32, device=DEV)
+    api.quantize_tokens_fp8(xt, q, s)
+    torch.cuda.synchronize()
+    qr, sr = omoe.quantize_groups(xt.float().cpu().numpy())
+    np.testing.assert_array_equal(q.cpu().numpy(), qr)
+    np.testing.assert_array_equal(s.cpu().numpy(), sr)
+
+
+@pytest.mark.parametrize("shared", [0, 1])
+def test_permute_without_gather_gives_the_same_indices(shared):
+    from split_weight_expert_amd import api
+    T, k, E, H = 517, 4, 37, 256
+    rng = np.random.default_rng(3)
+    idx_np = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    x = torch.randn(T, H, device=DEV).to(torch.bfloat16)
+    rows = T * k + shared * T
+    res = []
+    for with_rows in (True, False):
+        idx = torch.from_numpy(idx_np).to(DEV)
+        xp = torch.empty(rows, H, dtype=torch.bfloat16, device=DEV) if with_rows else None
+        off = torch.empty(E + shared + 1, dtype=torch.int32, device=DEV)
+        ps = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+        ip = torch.empty(T, k, dtype=torch.int32, device=DEV)
+        ws = torch.empty(api.workspace_bytes(api.OP_PERMUTE, T, k, E, H, 1, api.BF16, shared), dtype=torch.uint8,
+                         device=DEV)
+        api.permute(idx, E, shared, x, api.BF16, xp, None, off, ps, ip, ws)
+        torch.cuda.synchronize()
+        res.append((off.cpu().numpy(), ps.cpu().numpy(), ip.cpu().numpy()))
+    o, p, i = omoe.permute(idx_np, E, shared)[:3]
+    for r in res:
+        np.testing.assert_array_equal(r[0], o)
+        np.testing.assert_array_equal(r[1], p)
+        np.testing.assert_array_equal(r[2], i)
