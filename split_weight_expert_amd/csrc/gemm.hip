@@ -26,6 +26,8 @@
 //   * f32 (small shapes only): LDS-tiled FMA kernel with the same schedule.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -559,9 +561,11 @@ __device__ __forceinline__ int aslot(int row, int chunk) {
     return ROWB == 128 ? chunk ^ ((row >> 1) & 7) : chunk ^ ((row >> 2) & 3);
 }
 
-// Main loop and epilogue of one tile with MA active 32-row m-blocks (compile-time: the loop body is
-// straight-line code; only the LDS ring is waited on, and only here, with vmcnt).
-template <int BM, int ROWB, int MA, int KIND, bool FP8>
+// Main loop and epilogue of one tile with MA active 32-row m-blocks, of which this wave multiplies
+// MWV (compile-time: the loop body is straight-line code; only the LDS ring is waited on, and only
+// here, with vmcnt).  Every wave loads its share of the MA blocks' rows whatever its MWV, and a wave
+// with MWV == 0 only loads and keeps the barriers.
+template <int BM, int ROWB, int MA, int MWV, int KIND, bool FP8>
 __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c, uint8_t* smem,
                                           const float* s_bscale) {
     using C = FragCfg<BM, ROWB, FP8>;
@@ -571,14 +575,13 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     // only the rows of the MA active m-blocks are loaded: each wave DMAs an equal share of them
     constexpr int AI = loaded_rows<ROWB, MA, NW>() / NW / RPI;
     constexpr int PER = AI + AS + BIW;
-    // a wave multiplies MW m-blocks of its row part, or none when its part holds no active rows
-    constexpr int MW = MA < MIW ? MA : MIW;
+    constexpr bool active = MWV > 0;
+    constexpr int MW = active ? MWV : 1;               // accumulator blocks (one unused when idle)
     static_assert(AI >= 1 && loaded_rows<ROWB, MA, NW>() <= BM, "activation rows must split evenly over the waves");
-    static_assert(C::RH == 1 || MA <= MIW || MA % MIW == 0, "row parts are all active or all idle");
+    static_assert(MWV >= 0 && MWV <= MIW, "a wave holds at most its part's m-blocks");
     static_assert(PER * P < 64, "vmcnt budget");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cg = wave & 3, rh = C::RH == 1 ? 0 : wave >> 2;   // column group, row part
-    const bool active = rh * MIW < MA;
     const int rbase = rh * MIW * 32;                   // first tile row of this wave's part
     const int l32 = lane & 31, hi = lane >> 5;
     const Tile& t = c.t;
@@ -907,27 +910,46 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
         }
         __syncthreads();
     }
-    // active 32-row m-blocks (8-wave tiles: whole row parts)
+    // active 32-row m-blocks
     const int ma = (c.t.nrows + 31) / 32;
-    if constexpr (C::MI == 1) {
-        frag_tile<BM, ROWB, 1, KIND, FP8>(p, c, smem, s_bscale);
-    } else if constexpr (C::MI == 2) {
-        if (ma <= 1) frag_tile<BM, ROWB, 1, KIND, FP8>(p, c, smem, s_bscale);
-        else frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
-    } else if constexpr (C::MI == 4 && C::NW == 8) {
-        // two 64-row parts: one or both active
-        if (ma <= 2) frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
-        else frag_tile<BM, ROWB, 4, KIND, FP8>(p, c, smem, s_bscale);
-    } else if constexpr (C::MI == 4) {
-        if (ma <= 1) frag_tile<BM, ROWB, 1, KIND, FP8>(p, c, smem, s_bscale);
-        else if (ma == 2) frag_tile<BM, ROWB, 2, KIND, FP8>(p, c, smem, s_bscale);
-        else if (ma == 3) frag_tile<BM, ROWB, 3, KIND, FP8>(p, c, smem, s_bscale);
-        else frag_tile<BM, ROWB, 4, KIND, FP8>(p, c, smem, s_bscale);
+    if constexpr (C::NW == 4) {
+        if constexpr (C::MI == 1) {
+            frag_tile<BM, ROWB, 1, 1, KIND, FP8>(p, c, smem, s_bscale);
+        } else if constexpr (C::MI == 2) {
+            if (ma <= 1) frag_tile<BM, ROWB, 1, 1, KIND, FP8>(p, c, smem, s_bscale);
+            else frag_tile<BM, ROWB, 2, 2, KIND, FP8>(p, c, smem, s_bscale);
+        } else {
+            static_assert(C::MI == 4, "4-wave tiles hold at most 128 rows");
+            if (ma <= 1) frag_tile<BM, ROWB, 1, 1, KIND, FP8>(p, c, smem, s_bscale);
+            else if (ma == 2) frag_tile<BM, ROWB, 2, 2, KIND, FP8>(p, c, smem, s_bscale);
+            else if (ma == 3) frag_tile<BM, ROWB, 3, 3, KIND, FP8>(p, c, smem, s_bscale);
+            else frag_tile<BM, ROWB, 4, 4, KIND, FP8>(p, c, smem, s_bscale);
+        }
     } else {
-        static_assert(C::NW == 8, "256-row tiles run on 8 waves");
-        // two 128-row parts: one or both active
-        if (ma <= 4) frag_tile<BM, ROWB, 4, KIND, FP8>(p, c, smem, s_bscale);
-        else frag_tile<BM, ROWB, 8, KIND, FP8>(p, c, smem, s_bscale);
+        // two row parts of MIW m-blocks: the first part takes the first active blocks; a part without
+        // active rows runs the load-only variant (the same loads as the active part's)
+        constexpr int MIW = C::MIW;
+        const int rh = wave >> 2;
+        auto run = [&](auto tag) {
+            constexpr int MA = decltype(tag)::value;
+            constexpr int W0 = MA < MIW ? MA : MIW, W1 = MA > MIW ? MA - MIW : 0;
+            if (rh == 0) frag_tile<BM, ROWB, MA, W0, KIND, FP8>(p, c, smem, s_bscale);
+            else if constexpr (W1 > 0) frag_tile<BM, ROWB, MA, W1, KIND, FP8>(p, c, smem, s_bscale);
+            else frag_tile<BM, ROWB, MIW, 0, KIND, FP8>(p, c, smem, s_bscale);
+        };
+        if constexpr (MIW == 4) {
+            if (ma <= 1) run(std::integral_constant<int, 1>{});
+            else if (ma == 2) run(std::integral_constant<int, 2>{});
+            else if (ma <= 4) run(std::integral_constant<int, 4>{});
+            else if (ma <= 6) run(std::integral_constant<int, 6>{});
+            else run(std::integral_constant<int, 8>{});
+        } else {
+            static_assert(MIW == 2, "8-wave tiles are 128 (fp8) or 256 (bf16) rows");
+            if (ma <= 1) run(std::integral_constant<int, 1>{});
+            else if (ma == 2) run(std::integral_constant<int, 2>{});
+            else if (ma == 3) run(std::integral_constant<int, 3>{});
+            else run(std::integral_constant<int, 4>{});
+        }
     }
 }
 
