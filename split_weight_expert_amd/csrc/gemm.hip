@@ -130,17 +130,39 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
 }
 
 // ------------------------------------------------------------------------------ schedule
-// One workgroup: m-tile counts per group, their exclusive scan, and the m-tile table.
+// One workgroup: m-tile counts per group, their exclusive scan, and two m-tile tables over the same
+// tiles: `mtiles` in group order and `mtiles_by_size` with the groups taken by row count, largest
+// first (ties: lower group first; group order when G > kSortGroups).  bf16 GEMM1 walks the second:
+// tiles of similar length then share clusters, run in step and reuse each other's operands in L2.
+// GEMM2 was slower that way and keeps group order.
+constexpr int kSortGroups = 4096;
+
 template <int BM>
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int G,
-                                                        int32_t* __restrict__ mprefix, MTile* __restrict__ mtiles) {
+                                                        int32_t* __restrict__ mprefix, MTile* __restrict__ mtiles,
+                                                        MTile* __restrict__ mtiles_by_size) {
     __shared__ int wave_sum[16];
     __shared__ int carry_s;
+    __shared__ int order_s[kSortGroups];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool sorted = G <= kSortGroups;
+    if (sorted) {
+        for (int g = tid; g < G; g += 1024) {
+            const int n = offsets[g + 1] - offsets[g];
+            int rank = 0;
+            for (int h = 0; h < G; ++h) {
+                const int m = offsets[h + 1] - offsets[h];
+                rank += (m > n) || (m == n && h < g);
+            }
+            order_s[rank] = g;
+        }
+    }
+    for (int pass = 0; pass < 2; ++pass) {
+    MTile* table = pass == 0 ? mtiles : mtiles_by_size;
     if (tid == 0) carry_s = 0;
     __syncthreads();
     for (int base = 0; base < G; base += 1024) {
-        const int g = base + tid;
+        const int g = (pass == 1 && sorted && base + tid < G) ? order_s[base + tid] : base + tid;
         int c = 0;
         if (g < G) {
             const int n = offsets[g + 1] - offsets[g];
@@ -157,8 +179,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
         for (int w = 0; w < wave; ++w) before += wave_sum[w];
         const int excl = before + incl - c;
         if (g < G) {
-            mprefix[g] = excl;
-            for (int m = 0; m < c; ++m) mtiles[excl + m] = MTile{g, excl, c, 0};
+            if (pass == 0) mprefix[g] = excl;
+            for (int m = 0; m < c; ++m) table[excl + m] = MTile{g, excl, c, 0};
         }
         __syncthreads();
         if (tid == 0) {
@@ -168,7 +190,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
         }
         __syncthreads();
     }
-    if (tid == 0) mprefix[G] = carry_s;
+    if (pass == 0 && tid == 0) mprefix[G] = carry_s;
+    }
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
@@ -1077,7 +1100,7 @@ int choose_bm(int dtype, int64_t rows, int groups) {
 size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct FfnWs {
-    size_t a, a_scale, pre, mt, total;
+    size_t a, a_scale, pre, mt, mt_by_size, total;
 };
 
 // Workspace: A [rows, I] (+ fp8 scales), the m-tile prefix [G+1] and the m-tile table, sized for
@@ -1095,13 +1118,15 @@ FfnWs ffn_ws_layout(int64_t rows, int groups, int I, int dtype) {
     off += a256((size_t)(groups + 1) * 4);
     w.mt = off;
     off += a256((size_t)maxm * sizeof(MTile));
+    w.mt_by_size = off;
+    off += a256((size_t)maxm * sizeof(MTile));
     w.total = off;
     return w;
 }
 
 template <int BM>
-void launch_schedule(const int32_t* offsets, int G, int32_t* pre, MTile* mt, hipStream_t st) {
-    hipLaunchKernelGGL(schedule_kernel<BM>, dim3(1), dim3(1024), 0, st, offsets, G, pre, mt);
+void launch_schedule(const int32_t* offsets, int G, int32_t* pre, MTile* mt, MTile* mt_by_size, hipStream_t st) {
+    hipLaunchKernelGGL(schedule_kernel<BM>, dim3(1), dim3(1024), 0, st, offsets, G, pre, mt, mt_by_size);
 }
 
 // decode_tile deals clusters of kCluster tiles round-robin over the 8 XCDs, so the launch holds whole
@@ -1131,7 +1156,8 @@ void launch_dma(const GemmParams& p, int64_t tiles, hipStream_t st) {
 template <int BM>
 void launch_ffn(bool g1, bool g2, bool fp8_path, const int32_t* offsets, int G, const GemmParams& p1,
                 const GemmParams& p2, int64_t maxm, hipStream_t st) {
-    if (g1) launch_schedule<BM>(offsets, G, const_cast<int32_t*>(p1.mprefix), const_cast<MTile*>(p1.mtiles), st);
+    if (g1) launch_schedule<BM>(offsets, G, const_cast<int32_t*>(p1.mprefix), const_cast<MTile*>(p2.mtiles),
+                                const_cast<MTile*>(p1.mtiles), st);
     if constexpr (BM <= 128) {
         if (fp8_path) {
             if (g1) launch_dma<BM, kGemm1, true>(p1, maxm * p1.NT, st);
@@ -1223,7 +1249,9 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     p1.table = table;
     p1.offsets = offsets;
     p1.mprefix = reinterpret_cast<int32_t*>(base + L.pre);
-    p1.mtiles = reinterpret_cast<MTile*>(base + L.mt);
+    // bf16 GEMM1 walks the groups by size (measured ~1.5% faster at 8K tokens); fp8 GEMM1 was ~2%
+    // slower that way at 16K tokens and keeps group order
+    p1.mtiles = reinterpret_cast<MTile*>(base + (w_dtype == DWDP_BF16 ? L.mt_by_size : L.mt));
     p1.G = n_groups;
     p1.N = I;
     p1.K = H;
@@ -1233,6 +1261,7 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     p1.out_scale = reinterpret_cast<float*>(base + L.a_scale);
 
     GemmParams p2 = p1;
+    p2.mtiles = reinterpret_cast<MTile*>(base + L.mt);
     p2.a = base + L.a;
     p2.a_scale = reinterpret_cast<const float*>(base + L.a_scale);
     p2.a_rows = nullptr;
@@ -1247,7 +1276,8 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
 
     const bool g1 = stage != 2, g2 = stage != 1;
     if (w_dtype == DWDP_F32) {
-        if (g1) launch_schedule<kBmF32>(offsets, n_groups, const_cast<int32_t*>(p1.mprefix), const_cast<MTile*>(p1.mtiles), st);
+        if (g1) launch_schedule<kBmF32>(offsets, n_groups, const_cast<int32_t*>(p1.mprefix),
+                                        const_cast<MTile*>(p2.mtiles), const_cast<MTile*>(p1.mtiles), st);
         if (g1) launch_f32<kGemm1>(p1, maxm * p1.NT, st);
         if (g2) launch_f32<kGemm2>(p2, maxm * p2.NT, st);
     } else {
