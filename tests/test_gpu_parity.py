@@ -58,6 +58,8 @@ ROUTE_CASES = [
     ("decode64_bf16", dict(T=64, H=7168, E=256, k=8)),
     ("tiny_f32", dict(T=5, E=1, k=1)),
     ("tiny_f32", dict(T=9, E=8, k=8)),              # k = E
+    ("prefill8k_bf16", dict(T=130, H=512, E=1024, k=32)),   # the largest E and k the router takes
+    ("tiny_f32", dict(T=70, E=1024, k=1)),
 ]
 
 
@@ -529,3 +531,46 @@ def test_permute_without_gather_gives_the_same_indices(shared):
         np.testing.assert_array_equal(r[0], o)
         np.testing.assert_array_equal(r[1], p)
         np.testing.assert_array_equal(r[2], i)
+
+
+def test_grouped_ffn_with_more_groups_than_one_schedule_pass():
+    """1500 routed experts + a shared one: the tile schedule scans and sorts groups in several passes."""
+    from split_weight_expert_amd import ExpertStore, api
+    from split_weight_expert_amd.moe import DTYPES
+    cfg = shrink(synth.get_config("prefill8k_bf16"), T=400, H=256, I=128, E=1500, k=2, n_local=1500)
+    rng = np.random.default_rng(11)
+    idx_np = np.stack([rng.choice(cfg.E, cfg.k, replace=False) for _ in range(cfg.T)]).astype(np.int32)
+    idx_np[:40] = [3, 7]                                  # one group with 40+ rows
+    x = synth.tokens(cfg)
+    xt = torch.from_numpy(x).to(DEV, torch.bfloat16)
+    G = cfg.E + 1
+    store = ExpertStore(cfg.H, cfg.I, DTYPES["bf16"], [G], device=DEV)
+    used = sorted(set(idx_np.ravel().tolist()) | {cfg.E})
+    weights = {}
+    for e in used:
+        weights[e] = synth.expert_weights(cfg, e)
+        store.load(0, e, *(torch.from_numpy(a).to(DEV, torch.bfloat16) for a in weights[e]))
+    table = store.table([(0, g) for g in range(G)], DEV)
+    rows = cfg.T * (cfg.k + 1)
+    off = torch.empty(G + 1, dtype=torch.int32, device=DEV)
+    ps = torch.empty(rows, dtype=torch.int32, device=DEV)
+    ip = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=DEV)
+    wsp = torch.empty(api.workspace_bytes(api.OP_PERMUTE, cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, api.BF16, 1),
+                      dtype=torch.uint8, device=DEV)
+    api.permute(torch.from_numpy(idx_np).to(DEV), cfg.E, 1, xt, api.BF16, None, None, off, ps, ip, wsp)
+    y_perm = torch.empty(rows, cfg.H, dtype=torch.bfloat16, device=DEV)
+    wsf = torch.empty(api.workspace_bytes(api.OP_GROUPED_FFN, cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, api.BF16, 1),
+                      dtype=torch.uint8, device=DEV)
+    api.moe_grouped_ffn_tokens(0, table, G, off, ps, xt, None, cfg.H, cfg.I, api.BF16, y_perm, wsf)
+    torch.cuda.synchronize()
+    o, p, _, counts = omoe.permute(idx_np, cfg.E, 1)
+    np.testing.assert_array_equal(off.cpu().numpy(), o)
+    np.testing.assert_array_equal(ps.cpu().numpy(), p)
+    y = to_np(y_perm).astype(np.float64)
+    ref = np.zeros_like(y)
+    for g in used:
+        r0, r1 = o[g], o[g + 1]
+        if r1 > r0:
+            ref[r0:r1] = omoe.expert_ffn(omoe.prepare_tokens(x[p[r0:r1]], "bf16"),
+                                         *omoe.prepare_weights(*weights[g], "bf16"), "bf16")
+    assert_close(y, ref, "bf16", "grouped ffn, 1501 groups")
