@@ -41,8 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="FFN seconds the oracle's timed sample covers")
     ap.add_argument("--no-prefetch", action="store_true", help="skip the prefetch / overlap measurement")
-    ap.add_argument("--copy-workgroups", type=int, default=32)
-    ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy"])
+    ap.add_argument("--copy-workgroups", type=int, default=48)
+    ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy", "sdma"])
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run the slice-copy kernel on BYTES bytes (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -275,7 +275,7 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block):
 
     from split_weight_expert_amd import api
 
-    engine = api.COPY_KERNEL if args.copy_engine == "kernel" else api.COPY_HIPMEMCPY
+    engine = {"kernel": api.COPY_KERNEL, "hipmemcpy": api.COPY_HIPMEMCPY, "sdma": api.COPY_SDMA}[args.copy_engine]
     dst = layer.store.buffers[2].data_ptr()
     nbytes = sum(s[2] for s in layer.sources)
     cs = torch.cuda.Stream()

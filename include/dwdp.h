@@ -78,7 +78,10 @@ typedef enum {
 
 typedef enum {
     DWDP_COPY_HIPMEMCPY = 0,    /* one hipMemcpyAsync per slice, slices issued round-robin */
-    DWDP_COPY_KERNEL = 1        /* one launch of the library's slice-copy kernel walking the same plan */
+    DWDP_COPY_KERNEL = 1,       /* one launch of the library's slice-copy kernel walking the same plan */
+    DWDP_COPY_SDMA = 2          /* one hipMemcpyAsync per slice of kind hipMemcpyDeviceToDeviceNoCU: the
+                                   DMA engines move the bytes and no compute unit takes part, like the
+                                   copy engines of the pages' design */
 } dwdp_copy_engine;
 
 /* One entry of the per-expert pointer table (the split-weight "TensorList",
@@ -201,8 +204,8 @@ int dwdp_combine(const void* y_perm, const int32_t* inv_perm, const float* topk_
  * sources (slice c of every source before slice c+1 of any; the last slice of
  * a source may be short).  Destination ranges must not overlap.
  *   srcs: host array of n_src entries (1 <= n_src <= 64).
- *   engine: DWDP_COPY_HIPMEMCPY or DWDP_COPY_KERNEL; max_workgroups bounds the
- *   kernel engine's grid (0 = 32) and is ignored by the other engine.
+ *   engine: DWDP_COPY_HIPMEMCPY, DWDP_COPY_KERNEL or DWDP_COPY_SDMA; max_workgroups
+ *   bounds the kernel engine's grid (0 = 48) and is ignored by the other engines.
  *   wait_event (nullable): copy_stream waits on it first (the last reader of the
  *   destination slots).  done_event (nullable): recorded on copy_stream after
  *   the last slice. */

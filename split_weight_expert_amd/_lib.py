@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "lib", "libdwdp.so")
 DWDP_OK, DWDP_ERR_INVALID_ARG, DWDP_ERR_UNSUPPORTED, DWDP_ERR_WORKSPACE, DWDP_ERR_HIP = range(5)
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OP_PERMUTE, OP_GROUPED_FFN = 0, 1
-COPY_HIPMEMCPY, COPY_KERNEL = 0, 1
+COPY_HIPMEMCPY, COPY_KERNEL, COPY_SDMA = 0, 1, 2
 
 
 class ExpertPtrs(ctypes.Structure):

@@ -10,7 +10,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import BF16, COPY_HIPMEMCPY, COPY_KERNEL, F32, FP8_E4M3, OP_GROUPED_FFN, OP_PERMUTE  # noqa: F401
+from ._lib import BF16, COPY_HIPMEMCPY, COPY_KERNEL, COPY_SDMA, F32, FP8_E4M3, OP_GROUPED_FFN, OP_PERMUTE  # noqa: F401
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.uint8: FP8_E4M3}
 

@@ -144,7 +144,8 @@ extern "C" int dwdp_prefetch_chunks(void* dst, const dwdp_copy_src* srcs, int n_
     clear_error();
     int rc = check_sources(srcs, n_src, chunk_bytes);
     if (rc != DWDP_OK) return rc;
-    DWDP_REQUIRE(engine == DWDP_COPY_HIPMEMCPY || engine == DWDP_COPY_KERNEL, "unknown engine");
+    DWDP_REQUIRE(engine == DWDP_COPY_HIPMEMCPY || engine == DWDP_COPY_KERNEL || engine == DWDP_COPY_SDMA,
+                 "unknown engine");
     DWDP_REQUIRE(max_workgroups >= 0, "max_workgroups must be >= 0");
     hipStream_t st = as_stream(copy_stream);
     std::vector<dwdp_chunk> plan = make_plan(srcs, n_src, chunk_bytes);
@@ -173,14 +174,16 @@ extern "C" int dwdp_prefetch_chunks(void* dst, const dwdp_copy_src* srcs, int n_
         a.max_rounds = (int32_t)rounds;
     }
     if (wait_event) DWDP_HIP(hipStreamWaitEvent(st, reinterpret_cast<hipEvent_t>(wait_event), 0));
-    if (engine == DWDP_COPY_HIPMEMCPY) {
+    if (engine == DWDP_COPY_HIPMEMCPY || engine == DWDP_COPY_SDMA) {
+        // SDMA: the copy kind that keeps compute units out of it (the DMA engines move the bytes)
+        const hipMemcpyKind kind = engine == DWDP_COPY_SDMA ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
         for (const dwdp_chunk& c : plan) {
             DWDP_HIP(hipMemcpyAsync(static_cast<uint8_t*>(dst) + c.dst_offset,
-                                    static_cast<const uint8_t*>(srcs[c.source].src) + c.src_offset, c.bytes,
-                                    hipMemcpyDeviceToDevice, st));
+                                    static_cast<const uint8_t*>(srcs[c.source].src) + c.src_offset, c.bytes, kind,
+                                    st));
         }
     } else if (!plan.empty()) {
-        const int grid = (int)std::min<int64_t>(max_workgroups > 0 ? max_workgroups : 32, a.total_chunks);
+        const int grid = (int)std::min<int64_t>(max_workgroups > 0 ? max_workgroups : 48, a.total_chunks);
         hipLaunchKernelGGL(slice_copy_kernel, dim3(grid), dim3(256), 0, st, a);
         DWDP_LAUNCHED();
     }

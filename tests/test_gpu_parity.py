@@ -378,7 +378,7 @@ def test_combine_parity(dt, shared):
 
 # --------------------------------------------------------------------------------------- prefetch
 
-@pytest.mark.parametrize("engine", [0, 1])
+@pytest.mark.parametrize("engine", [0, 1, 2])
 def test_prefetch_copies_every_byte(engine):
     from split_weight_expert_amd import api
     rng = np.random.default_rng(engine)
