@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="FFN seconds the oracle's timed sample covers")
     ap.add_argument("--no-prefetch", action="store_true", help="skip the prefetch / overlap measurement")
+    ap.add_argument("--no-merge", action="store_true", help="skip the merge-copy ablation")
     ap.add_argument("--copy-workgroups", type=int, default=48)
     ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy", "sdma"])
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -262,11 +263,79 @@ def main():
 
     if want_prefetch:
         res["prefetch"] = measure_prefetch(layer, block, step, args, cfg, ms_step)
+    if not args.no_merge and cfg.n_prefetch > 0:
+        res["merge_ablation"] = measure_merge(layer, block, cfg, b, stage_ms)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def measure_merge(layer, block, cfg, b, stage_ms):
+    """The baseline the pointer table replaces: merge every group's record into one contiguous buffer
+    with a device-to-device copy (the library's slice-copy kernel on the whole GPU), then run the same
+    grouped FFN on it.  Reports the merge time next to the FFN on the split buffers."""
+    import torch
+
+    from split_weight_expert_amd import api
+
+    store = layer.store
+    G = cfg.E + cfg.shared
+    rec = store.rec
+    merged = torch.empty(G * rec, dtype=torch.uint8, device=layer.device)
+    # group order: resident experts, prefetched experts, then the shared expert (resident slot n_local)
+    srcs = [(store.buffers[0].data_ptr(), 0, cfg.n_local * rec),
+            (store.buffers[1].data_ptr(), cfg.n_local * rec, cfg.n_prefetch * rec)]
+    if cfg.shared:
+        srcs.append((store.buffers[0].data_ptr() + cfg.n_local * rec, cfg.E * rec, rec))
+    st = torch.cuda.current_stream()
+    table_m = api.table_to_device(api.fill_expert_table([merged.data_ptr()], [0] * G, list(range(G)), cfg.H, cfg.I,
+                                                        store.w_dtype), layer.device)
+
+    def merge():
+        api.prefetch_chunks(merged.data_ptr(), srcs, cfg.chunk_bytes, engine=api.COPY_KERNEL, max_workgroups=256,
+                            copy_stream=st)
+
+    merge()
+    block.ffn_stage(1, table_m, b)
+    block.ffn_stage(2, table_m, b)
+    torch.cuda.synchronize()
+    y_merged = b.y_perm.clone()
+    t_merge, t_ffn = [], []
+    for _ in range(5):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(st)
+        merge()
+        e[1].record(st)
+        block.ffn_stage(1, table_m, b)
+        block.ffn_stage(2, table_m, b)
+        e[2].record(st)
+        torch.cuda.synchronize()
+        t_merge.append(e[0].elapsed_time(e[1]))
+        t_ffn.append(e[1].elapsed_time(e[2]))
+    # the FFN alone on the merged buffer (no merge right before it)
+    t_alone = []
+    for _ in range(5):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(st)
+        block.ffn_stage(1, table_m, b)
+        block.ffn_stage(2, table_m, b)
+        e[1].record(st)
+        torch.cuda.synchronize()
+        t_alone.append(e[0].elapsed_time(e[1]))
+    # the same FFN through the split buffers must give the same bits
+    block.ffn_stage(1, layer.table(1), b)
+    block.ffn_stage(2, layer.table(1), b)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y_merged, b.y_perm))
+    ffn_split = stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]
+    m, f = float(np.median(t_merge)), float(np.median(t_ffn))
+    del merged
+    return dict(merged_bytes=G * rec, merge_ms=m, merge_gbps=G * rec / m / 1e6, ffn_ms_after_merge=f,
+                ffn_ms_merged=float(np.median(t_alone)), ffn_ms_split=ffn_split,
+                merge_plus_ffn_over_split=(m + f) / ffn_split, same_result=same,
+                note="merge = one slice-copy launch over all groups' records (256 workgroups)")
 
 
 def measure_prefetch(layer, block, step, args, cfg, ms_block):

@@ -574,3 +574,25 @@ def test_grouped_ffn_with_more_groups_than_one_schedule_pass():
             ref[r0:r1] = omoe.expert_ffn(omoe.prepare_tokens(x[p[r0:r1]], "bf16"),
                                          *omoe.prepare_weights(*weights[g], "bf16"), "bf16")
     assert_close(y, ref, "bf16", "grouped ffn, 1501 groups")
+
+
+def test_empty_batch_is_a_no_op_for_every_step():
+    """T = 0: every entry point returns OK and touches nothing."""
+    from split_weight_expert_amd import api
+    H, I, E, k = 256, 128, 8, 2
+    x = torch.empty(0, H, dtype=torch.bfloat16, device=DEV)
+    wr = torch.zeros(E, H, dtype=torch.bfloat16, device=DEV)
+    logits = torch.empty(0, E, device=DEV)
+    idx = torch.empty(0, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(0, k, device=DEV)
+    api.route_topk(x, wr, None, k, logits, idx, w)
+    off = torch.full((E + 2,), -5, dtype=torch.int32, device=DEV)
+    ps = torch.empty(0, dtype=torch.int32, device=DEV)
+    ws = torch.empty(4096, dtype=torch.uint8, device=DEV)
+    api.permute(idx, E, 1, x, api.BF16, None, None, off, ps, idx, ws)
+    api.quantize_tokens_fp8(x, torch.empty(0, H, dtype=torch.uint8, device=DEV),
+                            torch.empty(0, H // 128, device=DEV))
+    y = torch.empty(0, H, dtype=torch.bfloat16, device=DEV)
+    api.combine(torch.empty(0, H, dtype=torch.bfloat16, device=DEV), idx, w, 1, y)
+    torch.cuda.synchronize()
+    assert (off.cpu() == -5).all()         # T = 0 returns before anything is written
