@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-merge", action="store_true", help="skip the merge-copy ablation")
     ap.add_argument("--copy-workgroups", type=int, default=48)
     ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy", "sdma"])
+    ap.add_argument("--chunk-mib", type=float, default=0, help="prefetch slice size in MiB (default: the workload's 4)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run the slice-copy kernel on BYTES bytes (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -350,8 +351,10 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block):
     cs = torch.cuda.Stream()
     comp = torch.cuda.current_stream()
 
+    chunk = int(args.chunk_mib * (1 << 20)) if args.chunk_mib else cfg.chunk_bytes
+
     def copy(wait=None, done=None):
-        api.prefetch_chunks(dst, layer.sources, cfg.chunk_bytes, engine=engine, max_workgroups=args.copy_workgroups,
+        api.prefetch_chunks(dst, layer.sources, chunk, engine=engine, max_workgroups=args.copy_workgroups,
                             copy_stream=cs, wait_event=wait, done_event=done)
 
     reps = max(3, min(args.steps, 10))
@@ -384,8 +387,8 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block):
     per = cfg.n_prefetch // cfg.n_sources
     ok = bool(torch.equal(layer.store.record(2, per + 1), layer.src_store.record(1, 1)))
     c_alone = float(np.median(t_copy))
-    return dict(engine=args.copy_engine, workgroups=args.copy_workgroups, bytes=nbytes, chunk_bytes=cfg.chunk_bytes,
-                n_chunks=len(api.prefetch_plan(layer.sources, cfg.chunk_bytes)),
+    return dict(engine=args.copy_engine, workgroups=args.copy_workgroups, bytes=nbytes, chunk_bytes=chunk,
+                n_chunks=len(api.prefetch_plan(layer.sources, chunk)),
                 copy_ms=c_alone, copy_gbps=nbytes / c_alone / 1e6,
                 block_ms_alone=ms_block, block_ms_with_copy=float(np.median(t_blk)),
                 copy_ms_with_block=float(np.median(t_cp)), layer_ms_overlapped=float(np.median(t_tot)),
