@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="FFN seconds the oracle's timed sample covers")
     ap.add_argument("--no-prefetch", action="store_true", help="skip the prefetch / overlap measurement")
     ap.add_argument("--no-merge", action="store_true", help="skip the merge-copy ablation")
+    ap.add_argument("--pipeline-layers", type=int, default=0,
+                    help="also run this many layers back to back with ping-pong prefetch slots")
     ap.add_argument("--copy-workgroups", type=int, default=48)
     ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy", "sdma"])
     ap.add_argument("--chunk-mib", type=float, default=0, help="prefetch slice size in MiB (default: the workload's 4)")
@@ -264,6 +266,8 @@ def main():
 
     if want_prefetch:
         res["prefetch"] = measure_prefetch(layer, block, step, args, cfg, ms_step)
+    if args.pipeline_layers > 0 and want_prefetch:
+        res["pipeline"] = measure_pipeline(layer, block, step, args, cfg, res["prefetch"])
     if not args.no_merge and cfg.n_prefetch > 0:
         res["merge_ablation"] = measure_merge(layer, block, cfg, b, stage_ms)
 
@@ -337,6 +341,73 @@ def measure_merge(layer, block, cfg, b, stage_ms):
                 ffn_ms_merged=float(np.median(t_alone)), ffn_ms_split=ffn_split,
                 merge_plus_ffn_over_split=(m + f) / ffn_split, same_result=same,
                 note="merge = one slice-copy launch over all groups' records (256 workgroups)")
+
+
+def measure_pipeline(layer, block, step, args, cfg, pf):
+    """L layers back to back (DWDP paper summary §2): layer l reads prefetch slot set l % 2 while a side
+    stream fills slot set (l + 1) % 2 with layer l+1's non-local experts.  The copy into a slot set waits
+    for the event of the last layer that read it; a layer waits for the event of the copy that filled
+    its slot set (dwdp_prefetch_chunks' wait_event / done_event).  The source regions stand in for the
+    peers of every layer, so each layer's copy moves the same bytes.  Only the MoE block computes here
+    (no attention), so the copy has the block alone to hide behind: the conservative case.
+    """
+    import torch
+
+    from split_weight_expert_amd import api
+
+    L = args.pipeline_layers
+    engine = {"kernel": api.COPY_KERNEL, "hipmemcpy": api.COPY_HIPMEMCPY, "sdma": api.COPY_SDMA}[args.copy_engine]
+    chunk = int(args.chunk_mib * (1 << 20)) if args.chunk_mib else cfg.chunk_bytes
+    comp = torch.cuda.current_stream()
+    cs = torch.cuda.Stream()
+    tables = [layer.table(1), layer.table(2)]
+    dsts = [layer.store.buffers[1].data_ptr(), layer.store.buffers[2].data_ptr()]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b = block.buffers(cfg.T)
+
+    def run():
+        copy_done = [torch.cuda.Event(), torch.cuda.Event()]
+        compute_done = [torch.cuda.Event(), torch.cuda.Event()]
+        # layer 0's experts are in slot set 0 before the pipeline starts
+        api.prefetch_chunks(dsts[0], layer.sources, chunk, engine=engine, max_workgroups=args.copy_workgroups,
+                            copy_stream=cs, done_event=copy_done[0])
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        comp.wait_event(copy_done[0])
+        start.record(comp)
+        for l in range(L):
+            s, n = l % 2, (l + 1) % 2
+            if l + 1 < L:
+                # slot set n was last read by layer l-1 (nothing before layer 1)
+                api.prefetch_chunks(dsts[n], layer.sources, chunk, engine=engine,
+                                    max_workgroups=args.copy_workgroups, copy_stream=cs,
+                                    wait_event=compute_done[n] if l >= 1 else None, done_event=copy_done[n])
+            comp.wait_event(copy_done[s])
+            block.route(layer.x, layer.w_router, layer.bias, b)
+            block.permute(layer.x, b)
+            block.ffn_stage(1, tables[s], b)
+            block.ffn_stage(2, tables[s], b)
+            block.combine(b)
+            compute_done[s].record(comp)
+        end.record(comp)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    run()
+    t = float(np.median([run() for _ in range(3)]))
+    # compute alone per layer
+    e0.record()
+    for _ in range(L):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    tc = e0.elapsed_time(e1) / L
+    tp = pf["copy_ms"]
+    # both slot sets now hold the sources' bytes: spot-check one record of each
+    per = cfg.n_prefetch // cfg.n_sources
+    ok = all(bool(torch.equal(layer.store.record(k, per + 1), layer.src_store.record(1, 1))) for k in (1, 2))
+    return dict(layers=L, ms_per_layer=t / L, compute_ms_per_layer=tc, copy_ms_alone=tp, max_tc_tp=max(tc, tp),
+                layer_over_max=(t / L) / max(tc, tp), record_check=ok,
+                note="MoE block only (no attention); the copy of layer l+1 overlaps layer l")
 
 
 def measure_prefetch(layer, block, step, args, cfg, ms_block):
