@@ -8,22 +8,21 @@
 //
 // Structure
 //   * A tile schedule is built on the device from the group row offsets (no
-//     host round trip): every group is cut into BM-row m-tiles; tile `lin`
-//     of the (group, n-tile, m-tile) order -- m fastest, so the m-tiles that
-//     share one weight tile run back to back -- is found from lin / NT.
-//   * Workgroup ids are remapped so that each of the 8 XCDs (one 4 MB L2
-//     each) walks one contiguous stretch of that order: the m-tiles sharing a
-//     weight tile and the n-tiles sharing an activation tile are resident in
-//     the same L2 at the same time, so HBM sees each weight byte about once.
-//   * bf16 / fp8: both operands are K-contiguous; 128-byte row slices are
-//     staged through LDS (XOR-swizzled 16-byte chunks, double buffered,
-//     global loads for step k+1 in flight during the MFMAs of step k) and fed
-//     to v_mfma_f32_32x32x16_bf16 or v_mfma_scale_f32_32x32x64_f8f6f4 (unit
-//     scales).  fp8 keeps a per-128-K partial sum and folds it into the fp32
-//     accumulator with (row scale x block scale).
-//   * GEMM1's weight tile holds the gate rows and the up rows of the same
-//     output columns, so SwiGLU is applied in registers in the epilogue.
+//     host round trip): every group is cut into BM-row m-tiles, and two tables
+//     list them in group order and in group-size order (schedule_kernel).
+//   * Tiles reach the 8 XCDs in clusters of consecutive tiles dealt
+//     round-robin (decode_tile), so tiles that share a weight or activation
+//     slab run together on one XCD's L2.
+//   * bf16 / fp8 (gemm_frag_kernel): weights are stored fragment-major, every
+//     operand goes global -> LDS by DMA into a multi-stage ring, and the
+//     MFMAs are v_mfma_f32_32x32x16_bf16 or v_mfma_scale_f32_32x32x64_f8f6f4
+//     (unit scales, with a per-128-K fold of the fp32 block scales).  GEMM1's
+//     tile holds the gate and up rows of the same output columns, so SwiGLU
+//     (and for fp8 the re-quantisation of A) happens in the epilogue.
+//     GEMM1 reads its activation rows either from the permuted rows or from
+//     the token rows through perm_src.
 //   * f32 (small shapes only): LDS-tiled FMA kernel with the same schedule.
+//   * Router (bf16): router_mfma_kernel, a plain two-stage MFMA tile kernel.
 #include <algorithm>
 
 #include <type_traits>
@@ -196,60 +195,30 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// ------------------------------------------------------------------------------ MFMA kernel
-// BM x BN tile, WM x WN waves, 128 bytes of K per step (64 bf16 or 128 fp8 elements).
-template <int BM, int BN, int WM, int WN, int KIND, bool FP8>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(GemmParams p) {
+// ------------------------------------------------------------------------------ router kernel
+// logits [T, E] = x [T, H] * w_router[E, H]^T + bias, bf16 inputs and fp32 accumulation.  BM x BN tile,
+// WM x WN waves, 128 bytes (64 bf16) of K per step through a two-stage register-staged LDS buffer; rows
+// of both operands are swizzled in LDS (chunk c of row r at c ^ (r & 7)).
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void router_mfma_kernel(GemmParams p) {
     constexpr int NTHR = WM * WN * 64;
-    constexpr int ROWB = 128;
-    constexpr int KSTEP = FP8 ? 128 : 64;
+    constexpr int ROWB = 128, KSTEP = 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MI = TM / 32, NJ = TN / 32;
     constexpr int AC = BM * 8 / NTHR, BC = BN * 8 / NTHR;
     static_assert(AC >= 1 && BC >= 1 && BM * 8 % NTHR == 0 && BN * 8 % NTHR == 0, "tile / thread mismatch");
-    static_assert(KIND != kGemm1 || NJ % 2 == 0, "GEMM1 waves hold gate and up blocks in pairs");
 
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * ROWB];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * ROWB];
 
     Tile t;
-    if (!decode_tile<BM, KIND>(p, t)) return;
+    if (!decode_tile<BM, kRouter>(p, t)) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31, hi = lane >> 5;
-
-    const uint8_t* wbase;
-    const float* wscale = nullptr;
-    if (KIND == kGemm1) {
-        wbase = static_cast<const uint8_t*>(p.table[t.g].w13);
-        wscale = p.table[t.g].s13;
-    } else if (KIND == kGemm2) {
-        wbase = static_cast<const uint8_t*>(p.table[t.g].w2);
-        wscale = p.table[t.g].s2;
-    } else {
-        wbase = p.b_single;
-    }
-    const size_t ldk = (size_t)p.K * (FP8 ? 1 : 2);
+    const size_t ldk = (size_t)p.K * 2;
     const int KT = p.K / KSTEP;
-
-    // weight row held by tile row r
-    auto w_row = [&](int r) -> int {
-        if (KIND == kGemm1) {
-            constexpr int half = BN / 2;
-            const int n0 = t.nt * half;
-            return r < half ? n0 + r : p.I + n0 + (r - half);
-        }
-        return min(t.nt * BN + r, p.N - 1);
-    };
-    // tile row of the first row of the wave's n-block j
-    auto b_block_row = [&](int j) -> int {
-        if (KIND == kGemm1) {
-            constexpr int CW = BN / 2 / WN;
-            return j < NJ / 2 ? wn * CW + j * 32 : BN / 2 + wn * CW + (j - NJ / 2) * 32;
-        }
-        return wn * TN + j * 32;
-    };
 
     const uint8_t* ga[AC];
     int la[AC];
@@ -265,7 +234,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < BC; ++i) {
         const int lin = tid + i * NTHR, r = lin >> 3, c = lin & 7;
-        gb[i] = wbase + (size_t)w_row(r) * ldk + c * 16;
+        gb[i] = p.b_single + (size_t)min(t.nt * BN + r, p.N - 1) * ldk + c * 16;
         lb[i] = r * ROWB + ((c ^ (r & 7)) << 4);
     }
 
@@ -298,177 +267,49 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(GemmParams p) {
     auto lds16 = [&](const uint8_t* s, int row, int chunk) -> u32x4 {
         return *reinterpret_cast<const u32x4*>(&s[row * ROWB + ((chunk ^ (row & 7)) << 4)]);
     };
-
-    // fp8: per-row activation scales of this lane's accumulator rows
     auto row_of = [&](int i, int r) -> int { return wm * TM + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3); };
 
     gload(0);
     sstore(0);
     __syncthreads();
-
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
         if (kt + 1 < KT) gload(kt + 1);
         const uint8_t* A = sA[cur];
         const uint8_t* B = sB[cur];
-        if constexpr (!FP8) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int ch = s * 2 + hi;
-                bf16x8 af[MI], bf[NJ];
+        for (int s = 0; s < 4; ++s) {
+            const int ch = s * 2 + hi;
+            bf16x8 af[MI], bf[NJ];
 #pragma unroll
-                for (int i = 0; i < MI; ++i) af[i] = __builtin_bit_cast(bf16x8, lds16(A, wm * TM + i * 32 + l32, ch));
+            for (int i = 0; i < MI; ++i) af[i] = __builtin_bit_cast(bf16x8, lds16(A, wm * TM + i * 32 + l32, ch));
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) bf[j] = __builtin_bit_cast(bf16x8, lds16(B, b_block_row(j) + l32, ch));
-#pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    if (!m_act[i]) continue;
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-                }
-            }
-        } else {
-            f32x16 part[MI][NJ];
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int ch = s * 4 + hi * 2;
-                i32x8 af[MI], bf[NJ];
-#pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    const int row = wm * TM + i * 32 + l32;
-                    const u32x4 lo = lds16(A, row, ch), up = lds16(A, row, ch + 1);
-                    af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-                }
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const int row = b_block_row(j) + l32;
-                    const u32x4 lo = lds16(B, row, ch), up = lds16(B, row, ch + 1);
-                    bf[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-                }
-#pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    if (!m_act[i]) continue;
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j)
-                        part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], part[i][j], 0, 0, 0, 127,
-                                                                                     0, 127);
-                }
-            }
-            // fold this 128-wide K block: acc += part * (row scale * block scale)
-            const int KB = p.K / kFp8Group;
-            float sb[NJ];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) sb[j] = wscale[(size_t)(w_row(b_block_row(j)) / kFp8Group) * KB + kt];
+            for (int j = 0; j < NJ; ++j) bf[j] = __builtin_bit_cast(bf16x8, lds16(B, wn * TN + j * 32 + l32, ch));
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 if (!m_act[i]) continue;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rr = min(row_of(i, r), t.nrows - 1);
-                    const float sa = p.a_scale[(size_t)(t.row0 + rr) * KB + kt];
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) acc[i][j][r] += part[i][j][r] * (sa * sb[j]);
-                }
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
             }
         }
         if (kt + 1 < KT) sstore(cur ^ 1);
         __syncthreads();
     }
 
-    // ---------------------------------------------------------------- epilogue
-    if constexpr (KIND == kGemm1) {
-        constexpr int CW = BN / 2 / WN;          // A columns per wave
-        const int colA = t.nt * (BN / 2) + wn * CW;
-        if constexpr (!FP8) {
-            uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+    float* out = reinterpret_cast<float*>(p.out);
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int jb = 0; jb < NJ / 2; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = row_of(i, r);
-                        if (m < t.nrows) {
-                            const float a = silu_mul(acc[i][jb][r], acc[i][jb + NJ / 2][r]);
-                            out[(size_t)(t.row0 + m) * p.N + colA + jb * 32 + l32] = f32_to_bf16(a);
-                        }
-                    }
-        } else {
-            // A is quantised per row and 128-column group; the tile spans exactly one group.
-            static_assert(!FP8 || KIND != kGemm1 || BN / 2 == kFp8Group, "fp8 GEMM1 tile must cover one A group");
-            __shared__ float red[WN][BM];
-            float av[MI][NJ / 2][16];
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int jb = 0; jb < NJ / 2; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) av[i][jb][r] = silu_mul(acc[i][jb][r], acc[i][jb + NJ / 2][r]);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float m = 0.0f;
-#pragma unroll
-                    for (int jb = 0; jb < NJ / 2; ++jb) m = fmaxf(m, fabsf(av[i][jb][r]));
-#pragma unroll
-                    for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
-                    if (l32 == 0) red[wn][row_of(i, r)] = m;
-                }
-            __syncthreads();
-            uint8_t* out = p.out;
-            const int IB = p.N / kFp8Group;
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = row_of(i, r);
-                    float amax = 0.0f;
-#pragma unroll
-                    for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w][m]);
-                    const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
-                    if (m < t.nrows) {
-#pragma unroll
-                        for (int jb = 0; jb < NJ / 2; ++jb)
-                            out[(size_t)(t.row0 + m) * p.N + colA + jb * 32 + l32] = f32_to_e4m3(av[i][jb][r] / s);
-                        if (wn == 0 && l32 == 0) p.out_scale[(size_t)(t.row0 + m) * IB + t.nt] = s;
-                    }
-                }
-        }
-    } else if constexpr (KIND == kGemm2) {
-        uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+    for (int j = 0; j < NJ; ++j) {
+        const int col = t.nt * BN + wn * TN + j * 32 + l32;
+        if (col >= p.N) continue;
+        const float b = p.bias ? p.bias[col] : 0.0f;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = row_of(i, r);
-                    if (m < t.nrows)
-                        out[(size_t)(t.row0 + m) * p.N + t.nt * BN + wn * TN + j * 32 + l32] = f32_to_bf16(acc[i][j][r]);
-                }
-    } else {
-        float* out = reinterpret_cast<float*>(p.out);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int col = t.nt * BN + wn * TN + j * 32 + l32;
-            if (col >= p.N) continue;
-            const float b = p.bias ? p.bias[col] : 0.0f;
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = row_of(i, r);
-                    if (m < t.nrows) out[(size_t)(t.row0 + m) * p.N + col] = acc[i][j][r] + b;
-                }
-        }
+            for (int r = 0; r < 16; ++r) {
+                const int m = row_of(i, r);
+                if (m < t.nrows) out[(size_t)(t.row0 + m) * p.N + col] = acc[i][j][r] + b;
+            }
     }
 }
 
@@ -500,16 +341,6 @@ __device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds) {
 #endif
 }
 
-// 16-byte load through the global address space (the pointer comes out of the expert table, so the
-// compiler cannot infer it; a flat load would also count against lgkmcnt and serialise with LDS)
-__device__ __forceinline__ u32x4 gload16(const uint8_t* p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    return *(const __attribute__((address_space(1))) u32x4*)p;
-#else
-    return *reinterpret_cast<const u32x4*>(p);
-#endif
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -521,8 +352,6 @@ __device__ __forceinline__ void ordered_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
-
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 // Everything a tile needs once it is decoded.
 struct TileCtx {
@@ -1086,7 +915,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // Expert GEMMs (bf16, fp8): gemm_frag_kernel, BM x 256 tiles with BM = 32, 64, 128 or 256 (fp8: at
 // most 128) picked from the mean rows per group (decode batches give groups of a few rows).
 // f32: 64 x 64 FMA tiles.
-// Router (bf16): gemm_mfma_kernel, 64 x 64 tiles.
+// Router (bf16): router_mfma_kernel, 64 x 64 tiles.
 constexpr int kBnDma = 256;
 constexpr int kBmF32 = 64, kBnF32 = 64;
 constexpr int kBmRouter = 64, kBnRouter = 64;
@@ -1140,10 +969,10 @@ int64_t xcd_grid(int64_t tiles) {
     return (tiles + q - 1) / q * q;
 }
 
-template <int BM, int BN, int WM, int WN, int KIND, bool FP8>
-void launch_mfma(const GemmParams& p, int64_t tiles, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, KIND, FP8>), dim3((unsigned)xcd_grid(tiles)),
-                       dim3(WM * WN * 64), 0, st, p);
+template <int BM, int BN, int WM, int WN>
+void launch_router(const GemmParams& p, int64_t tiles, hipStream_t st) {
+    hipLaunchKernelGGL((router_mfma_kernel<BM, BN, WM, WN>), dim3((unsigned)xcd_grid(tiles)), dim3(WM * WN * 64), 0,
+                       st, p);
 }
 
 template <int KIND>
@@ -1198,7 +1027,7 @@ int router_gemm(const void* x, const void* w, int dtype, const float* bias, int6
     if (dtype == DWDP_BF16) {
         p.NT = (E + kBnRouter - 1) / kBnRouter;
         const int64_t grid = ((T + kBmRouter - 1) / kBmRouter) * p.NT;
-        launch_mfma<kBmRouter, kBnRouter, 2, 2, kRouter, false>(p, grid, st);
+        launch_router<kBmRouter, kBnRouter, 2, 2>(p, grid, st);
     } else {
         p.NT = (E + kBnF32 - 1) / kBnF32;
         const int64_t grid = ((T + kBmF32 - 1) / kBmF32) * p.NT;
