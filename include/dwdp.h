@@ -157,7 +157,8 @@ int dwdp_quantize_tokens_fp8(const void* x, int64_t T, int H, void* q, float* q_
  *   w_dtype F32: x_perm, weights and y_perm fp32, fp32 math.
  *   w_dtype BF16: x_perm and weights bf16, fp32 accumulation, A rounded to bf16,
  *     y_perm bf16.
- *   w_dtype FP8_E4M3: x_perm codes + x_perm_scale (see dwdp_permute), weights
+ *   w_dtype FP8_E4M3: x_perm codes + x_perm_scale (see dwdp_permute; 16-byte
+ *     aligned), weights
  *     codes + 128x128 block scales; products accumulated in fp32 per 128-wide K
  *     block and scaled by (row scale * block scale); A quantised per row and
  *     128-column group like x; y_perm bf16.

@@ -380,21 +380,21 @@ struct FragCfg {
     static constexpr int CH = ROWB / 16;                      // 16-byte chunks per activation row
     static constexpr int BF = ROWB / 32;                      // weight KB per n-block per step
     static constexpr int RPI = 1024 / ROWB;                   // activation rows per DMA instruction
-    static constexpr int SL = FP8 ? (BM + 63) / 64 : 0;       // fp8: 256-byte slices of row scales per step
-    static constexpr int AS = FP8 ? 1 : 0;                    // fp8: row-scale DMA instructions per wave per step
     static constexpr int BI = NJ * BF;                        // weight KB per column group per step
     static constexpr int BIW = BI / RH;                       // weight DMA instructions per wave per step
     static constexpr int ABYTES = BM * ROWB;
     static constexpr int BBYTES = 4 * BI * 1024;
-    static constexpr int STAGE = ABYTES + BBYTES + SL * 256;
-    static constexpr int EXTRA = FP8 ? NW * NJ * 64 * 4 : 0;  // fp8: weight block scales (K / 128 <= 64)
+    static constexpr int STAGE = ABYTES + BBYTES;
+    // fp8, outside the ring: the weight block scales of each wave's n-blocks and the tile's row scales
+    // (K / 128 <= 64 blocks each), both read once per tile
+    static constexpr int BSC = FP8 ? NW * NJ * 64 : 0;        // floats
+    static constexpr int EXTRA = FP8 ? (BSC + BM * 64) * 4 : 0;
     static constexpr int FIT = (163840 - EXTRA) / STAGE;
     static constexpr int NS = FIT < 8 ? FIT : 8;              // ring slots
     // bf16 reuses a slot one step after its last read (P = NS - 2), so the DMA can be issued before
     // the step's closing LDS wait; fp8 reuses it right after the barrier (P = NS - 1)
     static constexpr int P = FP8 ? NS - 1 : NS - 2;           // steps in flight ahead of the MFMAs
     static_assert(BM % 32 == 0 && (ROWB == 64 || ROWB == 128), "tile shape");
-    static_assert(!FP8 || SL <= NW, "every row-scale slice has a wave to load it");
     static_assert(P >= 1, "ring too shallow");
     static_assert(BI % RH == 0 && MI % RH == 0, "waves split the tile evenly");
 };
@@ -422,11 +422,11 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                                           const float* s_bscale) {
     using C = FragCfg<BM, ROWB, FP8>;
     constexpr int NS = C::NS, P = C::P, NJ = C::NJ, CH = C::CH, BF = C::BF, STAGE = C::STAGE;
-    constexpr int AS = C::AS, BI = C::BI, BIW = C::BIW, ABYTES = C::ABYTES, BBYTES = C::BBYTES;
+    constexpr int BI = C::BI, BIW = C::BIW, ABYTES = C::ABYTES, BBYTES = C::BBYTES;
     constexpr int RPI = C::RPI, NW = C::NW, MIW = C::MIW;
     // only the rows of the MA active m-blocks are loaded: each wave DMAs an equal share of them
     constexpr int AI = loaded_rows<ROWB, MA, NW>() / NW / RPI;
-    constexpr int PER = AI + AS + BIW;
+    constexpr int PER = AI + BIW;
     constexpr bool active = MWV > 0;
     constexpr int MW = active ? MWV : 1;               // accumulator blocks (one unused when idle)
     static_assert(AI >= 1 && loaded_rows<ROWB, MA, NW>() <= BM, "activation rows must split evenly over the waves");
@@ -446,16 +446,6 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         const int r = (wave * AI + i) * RPI + lane / CH;
         ga[i] = p.a + (size_t)act_row(p, t.row0 + min(r, t.nrows - 1)) * lda + aslot<ROWB>(r, lane % CH) * 16;
     }
-    // fp8: each wave loads one 256-byte slice (64 rows) of the step's row scales; slices repeat
-    // over the waves, so every wave issues the same count
-    [[maybe_unused]] const float* gs = nullptr;
-    [[maybe_unused]] int ls = 0;
-    if constexpr (FP8) {
-        const int KB = p.K / kFp8Group, sl = wave % C::SL;
-        gs = p.a_scale + (size_t)act_row(p, t.row0 + min(sl * 64 + lane, t.nrows - 1)) * KB;
-        ls = ABYTES + BBYTES + sl * 256;
-    }
-
     // this wave's share of its column group's weight fragments: BIW of the group's NJ * BF per step
     const uint8_t* gb[BIW];
     int lb[BIW];
@@ -480,10 +470,6 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         for (int i = 0; i < AI; ++i) dma16(ga[i] + (size_t)kt * ROWB, st + (wave * AI + i) * 1024);
 #pragma unroll
         for (int q = 0; q < BIW; ++q) dma16(gb[q] + (size_t)kt * BF * 1024, st + lb[q]);
-        if constexpr (FP8) {
-#pragma unroll
-            for (int i = 0; i < AS; ++i) dma4(reinterpret_cast<const uint8_t*>(gs + kt * ROWB / kFp8Group), st + ls);
-        }
     };
     auto a_frag = [&](const uint8_t* A, int i, int chunk) -> u32x4 {
         const int row = rbase + i * 32 + l32;
@@ -500,7 +486,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         const uint8_t* B = A + ABYTES;
         if constexpr (FP8) {
             if (!active) return;
-            const float* sa_lds = reinterpret_cast<const float*>(B + BBYTES);
+            const float* sa_lds = s_bscale + C::BSC + kt * BM;   // this K block's row scales
             float sb[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) sb[j] = s_bscale[(wave * NJ + j) * 64 + kt * ROWB / kFp8Group];
@@ -514,37 +500,54 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                     bf[j][s] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                                      (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
                 }
+            i32x8 af[MW][SH];
+            float sa[MW][16];
 #pragma unroll
             for (int i = 0; i < MW; ++i) {
-                i32x8 af[SH];
 #pragma unroll
                 for (int s = 0; s < SH; ++s) {
                     const u32x4 lo = a_frag(A, i, s * 4 + hi * 2), up = a_frag(A, i, s * 4 + hi * 2 + 1);
-                    af[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2],
-                                  (int)up[3]};
+                    af[i][s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1],
+                                     (int)up[2], (int)up[3]};
                 }
-                float sa[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float4 v = *reinterpret_cast<const float4*>(sa_lds + rbase + i * 32 + q * 8 + hi * 4);
-                    sa[4 * q] = v.x;
-                    sa[4 * q + 1] = v.y;
-                    sa[4 * q + 2] = v.z;
-                    sa[4 * q + 3] = v.w;
-                }
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    f32x16 part;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) part[r] = 0.0f;
-#pragma unroll
-                    for (int s = 0; s < SH; ++s)
-                        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[s], bf[j][s], part, 0, 0, 0, 127, 0,
-                                                                               127);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += part[r] * (sa[r] * sb[j]);
+                    sa[i][4 * q] = v.x;
+                    sa[i][4 * q + 1] = v.y;
+                    sa[i][4 * q + 2] = v.z;
+                    sa[i][4 * q + 3] = v.w;
                 }
             }
+            // The fold of an output block needs its MFMAs' result, so block b's fold is issued after
+            // block b+1's MFMAs: the VALU folds while the matrix core multiplies.  GEMM2's two n-blocks
+            // of a wave lie in one 128-row weight scale block (64 output columns, 64-aligned), so the
+            // row scale times the weight scale is formed once per row there.
+            f32x16 part[2];
+            auto fold = [&](int b) {
+                const int i = b / NJ, j = b % NJ;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] += part[b & 1][r] * (sa[i][r] * sb[KIND == kGemm2 ? 0 : j]);
+            };
+            auto mfma = [&](int b) {
+                const int i = b / NJ, j = b % NJ;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) part[b & 1][r] = 0.0f;
+#pragma unroll
+                for (int s = 0; s < SH; ++s)
+                    part[b & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i][s], bf[j][s], part[b & 1], 0, 0,
+                                                                                  0, 127, 0, 127);
+            };
+            constexpr int NB = MW * NJ;
+            mfma(0);
+#pragma unroll
+            for (int b = 1; b < NB; ++b) {
+                mfma(b);
+                fold(b - 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, SH, 0);   // block b's MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);   // block b-1's fold
+            }
+            fold(NB - 1);
         }
     };
 
@@ -763,6 +766,24 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
         for (int q = lane; q < 2 * KB; q += 64) {
             const int j = q / KB, kb = q % KB;
             s_bscale[(wave * 2 + j) * 64 + kb] = c.wscale[(size_t)(c.nblk[j] * 32 / kFp8Group) * KB + kb];
+        }
+        // the tile's row scales for every K block, stored K-block-major ([kb][row]) so that a lane's
+        // four consecutive rows are one 16-byte LDS read; a row's KB scales are contiguous in memory
+        constexpr int NT = C::NW * 64, PARTS = NT / BM;
+        static_assert(NT % BM == 0, "whole rows per thread group");
+        float* s_ascale = s_bscale + C::BSC;
+        const int row = threadIdx.x % BM, part = threadIdx.x / BM;
+        const float* src = p.a_scale + (size_t)act_row(p, c.t.row0 + min(row, c.t.nrows - 1)) * KB;
+        if (KB % 4 == 0) {
+            for (int k4 = part; k4 < KB / 4; k4 += PARTS) {
+                const float4 v = *reinterpret_cast<const float4*>(src + 4 * k4);
+                s_ascale[(4 * k4) * BM + row] = v.x;
+                s_ascale[(4 * k4 + 1) * BM + row] = v.y;
+                s_ascale[(4 * k4 + 2) * BM + row] = v.z;
+                s_ascale[(4 * k4 + 3) * BM + row] = v.w;
+            }
+        } else {
+            for (int kb = part; kb < KB; kb += PARTS) s_ascale[kb * BM + row] = src[kb];
         }
         __syncthreads();
     }
@@ -1065,7 +1086,8 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     DWDP_REQUIRE(aligned16(table) && aligned16(x) && aligned16(y_perm) && aligned16(ws),
                  "pointers must be 16-byte aligned");
     DWDP_REQUIRE(x_rows >= 1 && x_rows < ((int64_t)1 << 31), "x_rows out of range");
-    if (w_dtype == DWDP_FP8_E4M3) DWDP_REQUIRE(x_scale != nullptr, "fp8 needs the activation scales");
+    if (w_dtype == DWDP_FP8_E4M3)
+        DWDP_REQUIRE(x_scale != nullptr && aligned16(x_scale), "fp8 needs the activation scales, 16-byte aligned");
     FfnWs L = ffn_ws_layout(rows, n_groups, I, w_dtype);
     if (ws_bytes < L.total)
         return fail(DWDP_ERR_WORKSPACE, "dwdp_moe_grouped_ffn: workspace too small (need " + std::to_string(L.total) + ")");
