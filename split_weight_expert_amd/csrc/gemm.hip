@@ -471,6 +471,16 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
 #pragma unroll
         for (int q = 0; q < BIW; ++q) dma16(gb[q] + (size_t)kt * BF * 1024, st + lb[q]);
     };
+    // DMA instructions q0 .. q1-1 of a step's PER (activation rows first, then weight fragments)
+    auto issue_part = [&](int kt, int buf, int q0, int q1) {
+        uint8_t* st = smem + buf * STAGE;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (q < q0 || q >= q1) continue;
+            if (q < AI) dma16(ga[q] + (size_t)kt * ROWB, st + (wave * AI + q) * 1024);
+            else dma16(gb[q - AI] + (size_t)kt * BF * 1024, st + lb[q - AI]);
+        }
+    };
     auto a_frag = [&](const uint8_t* A, int i, int chunk) -> u32x4 {
         const int row = rbase + i * 32 + l32;
         return *reinterpret_cast<const u32x4*>(A + row * ROWB + (aslot<ROWB>(row, chunk) << 4));
@@ -481,11 +491,16 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     // fp8 step: per m-block, the two 64-wide halves of the 128-wide K block go through the scaled
     // MFMA (unit scales) into a fresh partial sum, which is folded into the accumulator with the
     // row scale times the weight block's scale.
-    auto compute = [&](int kt, int buf) {
+    // fp8 step kt; the DMA of step ikt into slot ibuf (when iss) is spread over its MFMA blocks, so a
+    // wave never waits for the memory pipe to accept its whole batch before its first MFMA
+    auto compute = [&](int kt, int buf, int ikt, int ibuf, bool iss) {
         const uint8_t* A = smem + buf * STAGE;
         const uint8_t* B = A + ABYTES;
         if constexpr (FP8) {
-            if (!active) return;
+            if (!active) {
+                if (iss) issue(ikt, ibuf);
+                return;
+            }
             const float* sa_lds = s_bscale + C::BSC + kt * BM;   // this K block's row scales
             float sb[NJ];
 #pragma unroll
@@ -538,13 +553,18 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                     part[b & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i][s], bf[j][s], part[b & 1], 0, 0,
                                                                                   0, 127, 0, 127);
             };
-            constexpr int NB = MW * NJ;
+            constexpr int NB = MW * NJ, QB = (PER + NB - 1) / NB;   // DMA instructions per block
             mfma(0);
+            if (iss) issue_part(ikt, ibuf, 0, QB);
+            __builtin_amdgcn_sched_group_barrier(0x008, SH, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, QB, 0);
 #pragma unroll
             for (int b = 1; b < NB; ++b) {
                 mfma(b);
+                if (iss) issue_part(ikt, ibuf, b * QB, (b + 1) * QB);
                 fold(b - 1);
                 __builtin_amdgcn_sched_group_barrier(0x008, SH, 0);   // block b's MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x020, QB, 0);   // part of the next DMA batch
                 __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);   // block b-1's fold
             }
             fold(NB - 1);
@@ -582,7 +602,6 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         // before the LDS wait, keeps the compiler's ds_read counting exact after the barrier.
         auto cross = [&](int kt, int u, bool steady) {
             __builtin_amdgcn_sched_barrier(0);   // keep the DMA (it rewrites M0) out of the MFMA region
-            if (steady || kt + 1 + P < KT) issue(kt + 1 + P, (u + 1 + P) % NS);
             __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
             // batch kt + 1 must have landed: the batches after it are kt+2 .. min(KT-1, kt+1+P)
             if (steady) {
@@ -608,13 +627,25 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
             }
         };
+        // with the DMA of batch kt + 1 + P spread over the first sub-step's MFMAs
+        auto interleave_dma = [&]() {
+#pragma unroll
+            for (int q = 0; q < NL; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, PERL, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+                if (q < PER) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // DMA
+            }
+        };
         auto step = [&](int kt, int u, bool steady) {
 #pragma unroll
             for (int sub = 0; sub < S; ++sub) {
                 if (sub + 1 < S) load(F[(sub + 1) & 1], u, sub + 1);
                 else if (steady || kt + 1 < KT) cross(kt, u, steady);
+                const bool dma = sub == 0 && (steady || kt + 1 + P < KT);
+                if (dma) issue(kt + 1 + P, (u + 1 + P) % NS);
                 mma(F[sub & 1]);
-                interleave();
+                if (sub == 0) interleave_dma();
+                else interleave();
             }
         };
         // prologue: batches 0 .. P into slots 0 .. P
@@ -645,8 +676,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
             for (int u = 0; u < NS; ++u) {
                 wait_vmcnt<(P - 1) * PER>();
                 ordered_barrier();
-                issue(k0 + u + P, (u + P) % NS);
-                compute(k0 + u, u);
+                compute(k0 + u, u, k0 + u + P, (u + P) % NS, true);
             }
         }
         // drain: at most NS + P - 1 steps, exact waits
@@ -662,8 +692,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                     wait_vmcnt<0>();
                 }
                 ordered_barrier();
-                if (kt + P < KT) issue(kt + P, (u + P) % NS);
-                compute(kt, u % NS);
+                compute(kt, u % NS, kt + P, (u + P) % NS, kt + P < KT);
             }
         }
     }
