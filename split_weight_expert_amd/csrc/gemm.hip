@@ -515,8 +515,11 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                     bf[j][s] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                                      (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
                 }
+            // fp8 blocks are computed transposed (weights as the MFMA's first operand): a lane then
+            // holds one row (token) of the block and 16 of its columns, all inside one 32-row weight
+            // n-block, so the fold's scale is a single product per lane and block.
             i32x8 af[MW][SH];
-            float sa[MW][16];
+            float sa[MW];
 #pragma unroll
             for (int i = 0; i < MW; ++i) {
 #pragma unroll
@@ -525,24 +528,16 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                     af[i][s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1],
                                      (int)up[2], (int)up[3]};
                 }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = *reinterpret_cast<const float4*>(sa_lds + rbase + i * 32 + q * 8 + hi * 4);
-                    sa[i][4 * q] = v.x;
-                    sa[i][4 * q + 1] = v.y;
-                    sa[i][4 * q + 2] = v.z;
-                    sa[i][4 * q + 3] = v.w;
-                }
+                sa[i] = sa_lds[rbase + i * 32 + l32];
             }
             // The fold of an output block needs its MFMAs' result, so block b's fold is issued after
-            // block b+1's MFMAs: the VALU folds while the matrix core multiplies.  GEMM2's two n-blocks
-            // of a wave lie in one 128-row weight scale block (64 output columns, 64-aligned), so the
-            // row scale times the weight scale is formed once per row there.
+            // block b+1's MFMAs: the VALU folds while the matrix core multiplies.
             f32x16 part[2];
             auto fold = [&](int b) {
                 const int i = b / NJ, j = b % NJ;
+                const float c = sa[i] * sb[j];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] += part[b & 1][r] * (sa[i][r] * sb[KIND == kGemm2 ? 0 : j]);
+                for (int r = 0; r < 16; ++r) acc[i][j][r] += part[b & 1][r] * c;
             };
             auto mfma = [&](int b) {
                 const int i = b / NJ, j = b % NJ;
@@ -550,10 +545,11 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                 for (int r = 0; r < 16; ++r) part[b & 1][r] = 0.0f;
 #pragma unroll
                 for (int s = 0; s < SH; ++s)
-                    part[b & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i][s], bf[j][s], part[b & 1], 0, 0,
+                    part[b & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j][s], af[i][s], part[b & 1], 0, 0,
                                                                                   0, 127, 0, 127);
             };
             constexpr int NB = MW * NJ, QB = (PER + NB - 1) / NB;   // DMA instructions per block
+            constexpr int NF = 17;                                  // VALU per fold
             mfma(0);
             if (iss) issue_part(ikt, ibuf, 0, QB);
             __builtin_amdgcn_sched_group_barrier(0x008, SH, 0);
@@ -565,7 +561,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                 fold(b - 1);
                 __builtin_amdgcn_sched_group_barrier(0x008, SH, 0);   // block b's MFMAs
                 __builtin_amdgcn_sched_group_barrier(0x020, QB, 0);   // part of the next DMA batch
-                __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);   // block b-1's fold
+                __builtin_amdgcn_sched_group_barrier(0x002, NF, 0);   // block b-1's fold
             }
             fold(NB - 1);
         }
@@ -711,38 +707,85 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                     if (m < t.nrows) out[(size_t)(t.row0 + m) * p.N + col] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
                 }
         } else {
-            // the tile's 128 A columns are exactly one quantisation group: amax over the 4 column groups
+            // Blocks are transposed: lane l32 holds row rbase + 32 i + l32 and element r holds A column
+            // cg * 32 + (r >> 2) * 8 + hi * 4 + (r & 3).  The tile's 128 A columns are exactly one
+            // quantisation group: the row's amax over its 4 column groups meets in LDS, then the codes
+            // go through LDS so that every row leaves as 128 contiguous bytes.
             ordered_barrier();                                   // every wave is done with the ring
             float* red = reinterpret_cast<float*>(smem);         // [4][BM]
+            uint8_t* codes = smem + 4 * BM * 4;                  // [BM][128], 16-byte chunks c at c ^ (row & 7)
             float av[MW][16];
             if (active) {
 #pragma unroll
-                for (int i = 0; i < MW; ++i)
+                for (int i = 0; i < MW; ++i) {
+                    float m = 0.0f;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         av[i][r] = silu_mul(acc[i][0][r], acc[i][1][r]);
-                        float m = fabsf(av[i][r]);
-#pragma unroll
-                        for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
-                        if (l32 == 0) red[cg * BM + row_of(i, r)] = m;
+                        m = fmaxf(m, fabsf(av[i][r]));
                     }
+                    m = fmaxf(m, __shfl_xor(m, 32));
+                    if (hi == 0) red[cg * BM + rbase + i * 32 + l32] = m;
+                }
             }
             __syncthreads();
-            const int IB = p.N / kFp8Group;
             if (active) {
+                const int IB = p.N / kFp8Group;
 #pragma unroll
-                for (int i = 0; i < MW; ++i)
+                for (int i = 0; i < MW; ++i) {
+                    const int m = rbase + i * 32 + l32;
+                    const float amax = fmaxf(fmaxf(red[m], red[BM + m]), fmaxf(red[2 * BM + m], red[3 * BM + m]));
+                    const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = row_of(i, r);
-                        const float amax = fmaxf(fmaxf(red[m], red[BM + m]), fmaxf(red[2 * BM + m], red[3 * BM + m]));
-                        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
-                        if (m < t.nrows) {
-                            p.out[(size_t)(t.row0 + m) * p.N + col] = f32_to_e4m3(av[i][r] / sc);
-                            if (cg == 0 && l32 == 0) p.out_scale[(size_t)(t.row0 + m) * IB + t.nt] = sc;
-                        }
+                    for (int q = 0; q < 4; ++q) {
+                        uint32_t w = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w |= (uint32_t)f32_to_e4m3(av[i][4 * q + e] / sc) << (8 * e);
+                        const int byte = cg * 32 + q * 8 + hi * 4;
+                        *reinterpret_cast<uint32_t*>(codes + m * 128 + (((byte >> 4) ^ (m & 7)) << 4) + (byte & 15)) = w;
+                    }
+                    if (cg == 0 && hi == 0 && m < t.nrows) p.out_scale[(size_t)(t.row0 + m) * IB + t.nt] = sc;
+                }
+            }
+            __syncthreads();
+            for (int q = threadIdx.x; q < BM * 8; q += NW * 64) {
+                const int row = q >> 3, c = q & 7;
+                if (row < t.nrows)
+                    *reinterpret_cast<u32x4*>(p.out + (size_t)(t.row0 + row) * p.N + t.nt * 128 + c * 16) =
+                        *reinterpret_cast<const u32x4*>(codes + row * 128 + ((c ^ (row & 7)) << 4));
+            }
+        }
+    } else if constexpr (FP8) {
+        // Blocks are transposed (lane l32 holds a row, element r holds column (r >> 2) * 8 + hi * 4 +
+        // (r & 3) of n-block j): the tile's bf16 rows go through LDS and leave in 16-byte pieces.
+        ordered_barrier();                                       // every wave is done with the ring
+        uint8_t* stg = smem;                                     // [BM][512 B], chunks c at c ^ (row & 31)
+        if (active) {
+#pragma unroll
+            for (int i = 0; i < MW; ++i) {
+                const int m = rbase + i * 32 + l32;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t w0 = (uint32_t)f32_to_bf16(acc[i][j][4 * q]) |
+                                            ((uint32_t)f32_to_bf16(acc[i][j][4 * q + 1]) << 16);
+                        const uint32_t w1 = (uint32_t)f32_to_bf16(acc[i][j][4 * q + 2]) |
+                                            ((uint32_t)f32_to_bf16(acc[i][j][4 * q + 3]) << 16);
+                        const int byte = (cg * 64 + j * 32 + q * 8 + hi * 4) * 2;
+                        uint32_t* d = reinterpret_cast<uint32_t*>(stg + m * 512 + (((byte >> 4) ^ (m & 31)) << 4) + (byte & 15));
+                        d[0] = w0;
+                        d[1] = w1;
                     }
             }
+        }
+        __syncthreads();
+        uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+        for (int q = threadIdx.x; q < BM * 32; q += NW * 64) {
+            const int row = q >> 5, c = q & 31;
+            if (row < t.nrows)
+                *reinterpret_cast<u32x4*>(out + (size_t)(t.row0 + row) * p.N + t.nt * 256 + c * 8) =
+                    *reinterpret_cast<const u32x4*>(stg + row * 512 + ((c ^ (row & 31)) << 4));
         }
     } else if (active) {
         uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
