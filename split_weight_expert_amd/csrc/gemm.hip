@@ -591,7 +591,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
             for (int i = 0; i < MW; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
         };
         // End of step kt (ring slot u) into step kt + 1.  Batch kt + 1 + P goes to the slot of step
         // kt - 1, which every wave stopped reading before the previous barrier; issuing it here, just
@@ -694,18 +694,40 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     }
 
     // ---------------------------------------------------------------- epilogue
-    auto row_of = [&](int i, int r) -> int { return rbase + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3); };
     if constexpr (KIND == kGemm1) {
-        const int col = t.nt * 128 + cg * 32 + l32;       // A column of this lane
         if constexpr (!FP8) {
-            uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+            // Blocks are transposed (lane l32 holds row rbase + 32 i + l32, element r holds A column
+            // cg * 32 + (r >> 2) * 8 + hi * 4 + (r & 3)): A's bf16 rows go through LDS and leave in
+            // 16-byte pieces.
+            ordered_barrier();                                   // every wave is done with the ring
+            uint8_t* stg = smem;                                 // [BM][256 B], chunks c at c ^ (row & 15)
+            if (active) {
 #pragma unroll
-            for (int i = 0; i < MW; ++i)
+                for (int i = 0; i < MW; ++i) {
+                    const int m = rbase + i * 32 + l32;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = row_of(i, r);
-                    if (m < t.nrows) out[(size_t)(t.row0 + m) * p.N + col] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
+                    for (int q = 0; q < 4; ++q) {
+                        uint32_t w[2];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            w[h] = (uint32_t)f32_to_bf16(silu_mul(acc[i][0][4 * q + 2 * h], acc[i][1][4 * q + 2 * h])) |
+                                   ((uint32_t)f32_to_bf16(silu_mul(acc[i][0][4 * q + 2 * h + 1], acc[i][1][4 * q + 2 * h + 1]))
+                                    << 16);
+                        const int byte = (cg * 32 + q * 8 + hi * 4) * 2;
+                        uint32_t* d = reinterpret_cast<uint32_t*>(stg + m * 256 + (((byte >> 4) ^ (m & 15)) << 4) + (byte & 15));
+                        d[0] = w[0];
+                        d[1] = w[1];
+                    }
                 }
+            }
+            __syncthreads();
+            uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+            for (int q = threadIdx.x; q < BM * 16; q += NW * 64) {
+                const int row = q >> 4, c = q & 15;
+                if (row < t.nrows)
+                    *reinterpret_cast<u32x4*>(out + (size_t)(t.row0 + row) * p.N + t.nt * 128 + c * 8) =
+                        *reinterpret_cast<const u32x4*>(stg + row * 256 + ((c ^ (row & 15)) << 4));
+            }
         } else {
             // Blocks are transposed: lane l32 holds row rbase + 32 i + l32 and element r holds A column
             // cg * 32 + (r >> 2) * 8 + hi * 4 + (r & 3).  The tile's 128 A columns are exactly one
@@ -755,7 +777,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                         *reinterpret_cast<const u32x4*>(codes + row * 128 + ((c ^ (row & 7)) << 4));
             }
         }
-    } else if constexpr (FP8) {
+    } else {
         // Blocks are transposed (lane l32 holds a row, element r holds column (r >> 2) * 8 + hi * 4 +
         // (r & 3) of n-block j): the tile's bf16 rows go through LDS and leave in 16-byte pieces.
         ordered_barrier();                                       // every wave is done with the ring
@@ -787,18 +809,6 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                 *reinterpret_cast<u32x4*>(out + (size_t)(t.row0 + row) * p.N + t.nt * 256 + c * 8) =
                     *reinterpret_cast<const u32x4*>(stg + row * 512 + ((c ^ (row & 31)) << 4));
         }
-    } else if (active) {
-        uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
-#pragma unroll
-        for (int i = 0; i < MW; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = row_of(i, r);
-                    if (m < t.nrows)
-                        out[(size_t)(t.row0 + m) * p.N + t.nt * 256 + cg * 64 + j * 32 + l32] = f32_to_bf16(acc[i][j][r]);
-                }
     }
 }
 
