@@ -384,11 +384,15 @@ struct FragCfg {
     static constexpr int BIW = BI / RH;                       // weight DMA instructions per wave per step
     static constexpr int ABYTES = BM * ROWB;
     static constexpr int BBYTES = 4 * BI * 1024;
-    static constexpr int STAGE = ABYTES + BBYTES;
-    // fp8, outside the ring: the weight block scales of each wave's n-blocks and the tile's row scales
-    // (K / 128 <= 64 blocks each), both read once per tile
+    // fp8: a step's slot also holds the row scales of its K block.  Each wave loads those of RW rows
+    // with one 64-lane DMA instruction into a 64-float slice of its own (lanes past RW repeat the
+    // last row), so row R's scale sits at float (R / RW) * 64 + R % RW.
+    static constexpr int RW = BM / NW;
+    static constexpr int STAGE = ABYTES + BBYTES + (FP8 ? NW * 64 * 4 : 0);
+    // fp8, outside the ring: the weight block scales of each wave's n-blocks (K / 128 <= 64), read
+    // once per tile
     static constexpr int BSC = FP8 ? NW * NJ * 64 : 0;        // floats
-    static constexpr int EXTRA = FP8 ? (BSC + BM * 64) * 4 : 0;
+    static constexpr int EXTRA = BSC * 4;
     static constexpr int FIT = (163840 - EXTRA) / STAGE;
     static constexpr int NS = FIT < 8 ? FIT : 8;              // ring slots
     // bf16 reuses a slot one step after its last read (P = NS - 2), so the DMA can be issued before
@@ -426,7 +430,8 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     constexpr int RPI = C::RPI, NW = C::NW, MIW = C::MIW;
     // only the rows of the MA active m-blocks are loaded: each wave DMAs an equal share of them
     constexpr int AI = loaded_rows<ROWB, MA, NW>() / NW / RPI;
-    constexpr int PER = AI + BIW;
+    constexpr int AS = FP8 ? 1 : 0;                    // row-scale DMA instructions per step
+    constexpr int PER = AI + BIW + AS;
     constexpr bool active = MWV > 0;
     constexpr int MW = active ? MWV : 1;               // accumulator blocks (one unused when idle)
     static_assert(AI >= 1 && loaded_rows<ROWB, MA, NW>() <= BM, "activation rows must split evenly over the waves");
@@ -440,6 +445,10 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     const int KT = c.KT;
     const size_t lda = (size_t)p.K * (FP8 ? 1 : 2);
 
+    // fp8: this wave's RW rows of the step's row scales (lanes RW.. idle)
+    [[maybe_unused]] const float* gs = nullptr;
+    if constexpr (FP8)
+        gs = p.a_scale + (size_t)act_row(p, t.row0 + min(wave * C::RW + min(lane, C::RW - 1), t.nrows - 1)) * (p.K / kFp8Group);
     const uint8_t* ga[AI];
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
@@ -464,21 +473,26 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    [[maybe_unused]] auto scale_dma = [&](int kt, uint8_t* st) {
+        dma4(reinterpret_cast<const uint8_t*>(gs + kt), st + ABYTES + BBYTES + wave * 256);
+    };
     auto issue = [&](int kt, int buf) {
         uint8_t* st = smem + buf * STAGE;
 #pragma unroll
         for (int i = 0; i < AI; ++i) dma16(ga[i] + (size_t)kt * ROWB, st + (wave * AI + i) * 1024);
 #pragma unroll
         for (int q = 0; q < BIW; ++q) dma16(gb[q] + (size_t)kt * BF * 1024, st + lb[q]);
+        if constexpr (FP8) scale_dma(kt, st);
     };
-    // DMA instructions q0 .. q1-1 of a step's PER (activation rows first, then weight fragments)
+    // DMA instructions q0 .. q1-1 of a step's PER (activation rows, weight fragments, row scales)
     auto issue_part = [&](int kt, int buf, int q0, int q1) {
         uint8_t* st = smem + buf * STAGE;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             if (q < q0 || q >= q1) continue;
             if (q < AI) dma16(ga[q] + (size_t)kt * ROWB, st + (wave * AI + q) * 1024);
-            else dma16(gb[q - AI] + (size_t)kt * BF * 1024, st + lb[q - AI]);
+            else if (q < AI + BIW) dma16(gb[q - AI] + (size_t)kt * BF * 1024, st + lb[q - AI]);
+            else if constexpr (FP8) scale_dma(kt, st);
         }
     };
     auto a_frag = [&](const uint8_t* A, int i, int chunk) -> u32x4 {
@@ -501,7 +515,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                 if (iss) issue(ikt, ibuf);
                 return;
             }
-            const float* sa_lds = s_bscale + C::BSC + kt * BM;   // this K block's row scales
+            const float* sa_lds = reinterpret_cast<const float*>(B + BBYTES);   // this K block's row scales
             float sb[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) sb[j] = s_bscale[(wave * NJ + j) * 64 + kt * ROWB / kFp8Group];
@@ -528,7 +542,8 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                     af[i][s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1],
                                      (int)up[2], (int)up[3]};
                 }
-                sa[i] = sa_lds[rbase + i * 32 + l32];
+                const int R = rbase + i * 32 + l32;
+                sa[i] = sa_lds[(R / C::RW) * 64 + R % C::RW];
             }
             // The fold of an output block needs its MFMAs' result, so block b's fold is issued after
             // block b+1's MFMAs: the VALU folds while the matrix core multiplies.
@@ -848,24 +863,6 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
         for (int q = lane; q < 2 * KB; q += 64) {
             const int j = q / KB, kb = q % KB;
             s_bscale[(wave * 2 + j) * 64 + kb] = c.wscale[(size_t)(c.nblk[j] * 32 / kFp8Group) * KB + kb];
-        }
-        // the tile's row scales for every K block, stored K-block-major ([kb][row]) so that a lane's
-        // four consecutive rows are one 16-byte LDS read; a row's KB scales are contiguous in memory
-        constexpr int NT = C::NW * 64, PARTS = NT / BM;
-        static_assert(NT % BM == 0, "whole rows per thread group");
-        float* s_ascale = s_bscale + C::BSC;
-        const int row = threadIdx.x % BM, part = threadIdx.x / BM;
-        const float* src = p.a_scale + (size_t)act_row(p, c.t.row0 + min(row, c.t.nrows - 1)) * KB;
-        if (KB % 4 == 0) {
-            for (int k4 = part; k4 < KB / 4; k4 += PARTS) {
-                const float4 v = *reinterpret_cast<const float4*>(src + 4 * k4);
-                s_ascale[(4 * k4) * BM + row] = v.x;
-                s_ascale[(4 * k4 + 1) * BM + row] = v.y;
-                s_ascale[(4 * k4 + 2) * BM + row] = v.z;
-                s_ascale[(4 * k4 + 3) * BM + row] = v.w;
-            }
-        } else {
-            for (int kb = part; kb < KB; kb += PARTS) s_ascale[kb * BM + row] = src[kb];
         }
         __syncthreads();
     }
