@@ -836,9 +836,8 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
 
     TileCtx c;
     if (!decode_tile<BM, KIND>(p, c.t)) return;
-    // Above the default wave priority: when the layer-ahead prefetch copy runs beside the block, the
-    // GEMM's waves win the arbitration on CUs both occupy (measured at 16K fp8 tokens: the block's
-    // slowdown beside the copy drops from 13% to 9%; alone it makes no difference).
+    // Above the default wave priority, so that the GEMM's waves win the arbitration on a CU that also
+    // hosts waves of another kernel (the layer-ahead prefetch copy); alone it makes no difference.
     __builtin_amdgcn_s_setprio(2);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     c.KT = p.K / (FP8 ? ROWB : ROWB / 2);
@@ -1088,9 +1087,8 @@ void launch_dma(const GemmParams& p, int64_t tiles, hipStream_t st) {
 
 template <int BM>
 void launch_ffn(bool g1, bool g2, bool fp8_path, const int32_t* offsets, int G, const GemmParams& p1,
-                const GemmParams& p2, int64_t maxm, hipStream_t st) {
-    if (g1) launch_schedule<BM>(offsets, G, const_cast<int32_t*>(p1.mprefix), const_cast<MTile*>(p2.mtiles),
-                                const_cast<MTile*>(p1.mtiles), st);
+                const GemmParams& p2, MTile* mt_group, MTile* mt_size, int64_t maxm, hipStream_t st) {
+    if (g1) launch_schedule<BM>(offsets, G, const_cast<int32_t*>(p1.mprefix), mt_group, mt_size, st);
     if constexpr (BM <= 128) {
         if (fp8_path) {
             if (g1) launch_dma<BM, kGemm1, true>(p1, maxm * p1.NT, st);
@@ -1183,9 +1181,11 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     p1.table = table;
     p1.offsets = offsets;
     p1.mprefix = reinterpret_cast<int32_t*>(base + L.pre);
-    // bf16 GEMM1 walks the groups by size (measured ~1.5% faster at 8K tokens); fp8 GEMM1 was ~2%
-    // slower that way at 16K tokens and keeps group order
-    p1.mtiles = reinterpret_cast<MTile*>(base + (w_dtype == DWDP_BF16 ? L.mt_by_size : L.mt));
+    // GEMM1 walks the groups by size (bf16: measured ~1.5% faster at 8K tokens).  GEMM2 keeps group
+    // order for bf16 (slower by size) and walks by size otherwise.  The order moves no result bit.
+    MTile* mt_group = reinterpret_cast<MTile*>(base + L.mt);
+    MTile* mt_size = reinterpret_cast<MTile*>(base + L.mt_by_size);
+    p1.mtiles = mt_size;
     p1.G = n_groups;
     p1.N = I;
     p1.K = H;
@@ -1195,7 +1195,7 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     p1.out_scale = reinterpret_cast<float*>(base + L.a_scale);
 
     GemmParams p2 = p1;
-    p2.mtiles = reinterpret_cast<MTile*>(base + L.mt);
+    p2.mtiles = w_dtype == DWDP_BF16 ? mt_group : mt_size;
     p2.a = base + L.a;
     p2.a_scale = reinterpret_cast<const float*>(base + L.a_scale);
     p2.a_rows = nullptr;
@@ -1210,16 +1210,15 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
 
     const bool g1 = stage != 2, g2 = stage != 1;
     if (w_dtype == DWDP_F32) {
-        if (g1) launch_schedule<kBmF32>(offsets, n_groups, const_cast<int32_t*>(p1.mprefix),
-                                        const_cast<MTile*>(p2.mtiles), const_cast<MTile*>(p1.mtiles), st);
+        if (g1) launch_schedule<kBmF32>(offsets, n_groups, const_cast<int32_t*>(p1.mprefix), mt_group, mt_size, st);
         if (g1) launch_f32<kGemm1>(p1, maxm * p1.NT, st);
         if (g2) launch_f32<kGemm2>(p2, maxm * p2.NT, st);
     } else {
         const bool fp8 = w_dtype == DWDP_FP8_E4M3;
-        if (bm == 256) launch_ffn<256>(g1, g2, false, offsets, n_groups, p1, p2, maxm, st);
-        else if (bm == 128) launch_ffn<128>(g1, g2, fp8, offsets, n_groups, p1, p2, maxm, st);
-        else if (bm == 64) launch_ffn<64>(g1, g2, fp8, offsets, n_groups, p1, p2, maxm, st);
-        else launch_ffn<32>(g1, g2, fp8, offsets, n_groups, p1, p2, maxm, st);
+        if (bm == 256) launch_ffn<256>(g1, g2, false, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
+        else if (bm == 128) launch_ffn<128>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
+        else if (bm == 64) launch_ffn<64>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
+        else launch_ffn<32>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
     }
     DWDP_LAUNCHED();
     return DWDP_OK;
