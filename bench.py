@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--copy-workgroups", type=int, default=48)
     ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy", "sdma"])
     ap.add_argument("--chunk-mib", type=float, default=0, help="prefetch slice size in MiB (default: the workload's 4)")
+    ap.add_argument("--smi", action="store_true",
+                    help="also sample GPU clock and power (amd-smi) while the block runs alone, beside the "
+                         "copy and beside a one-workgroup copy")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run the slice-copy kernel on BYTES bytes (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -266,6 +269,8 @@ def main():
 
     if want_prefetch:
         res["prefetch"] = measure_prefetch(layer, block, step, args, cfg, ms_step)
+        if args.smi:
+            res["prefetch"]["smi"] = measure_smi(layer, step, args, cfg)
     if args.pipeline_layers > 0 and want_prefetch:
         res["pipeline"] = measure_pipeline(layer, block, step, args, cfg, res["prefetch"])
     if not args.no_merge and cfg.n_prefetch > 0:
@@ -466,6 +471,75 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block):
                 slowdown=float(np.median(t_blk)) / ms_block - 1.0,
                 hidden=bool(np.median(t_cp) <= np.median(t_blk)), record_check=ok,
                 note="stand-in source regions sit in the same HBM, so the copy reads and writes locally")
+
+
+def measure_smi(layer, step, args, cfg, secs=2.5):
+    """GPU clock and socket power (amd-smi, sampled from a thread) while the block runs back to back:
+    alone, beside the prefetch copy (args.copy_workgroups) started with every block, and beside one
+    long copy of a single workgroup.  Tells a clock (DVFS) slowdown from a contention one."""
+    import subprocess
+    import threading
+
+    import torch
+
+    from split_weight_expert_amd import api
+
+    dst = layer.store.buffers[2].data_ptr()
+    cs = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            t0 = time.time()
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+                g = json.loads(r.stdout)["gpu_data"][0]
+                clk = [g["clock"][k]["clk"]["value"] for k in g["clock"] if k.startswith("gfx_")]
+                samples.append(((t0 + time.time()) / 2, float(g["power"]["socket_power"]["value"]),
+                                float(np.mean(clk))))
+            except Exception:
+                return
+
+    def copy(wg):
+        s = torch.cuda.Event()
+        s.record(comp)
+        api.prefetch_chunks(dst, layer.sources, cfg.chunk_bytes, engine=api.COPY_KERNEL, max_workgroups=wg,
+                            copy_stream=cs, wait_event=s)
+
+    def phase(name, with_copy):
+        t0 = time.time()
+        ms = []
+        while time.time() - t0 < secs:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if with_copy > 1:
+                copy(with_copy)
+            elif with_copy == 1 and cs.query():
+                copy(1)                               # one workgroup, kept running beside the blocks
+            e0.record(comp)
+            step()
+            e1.record(comp)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+            if with_copy > 1:
+                cs.synchronize()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        sel = [x for x in samples if t0 + 0.3 < x[0] < t1]
+        return name, dict(block_ms=float(np.median(ms)), blocks=len(ms), samples=len(sel),
+                          power_w=float(np.median([x[1] for x in sel])) if sel else None,
+                          gfx_mhz=float(np.median([x[2] for x in sel])) if sel else None)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(1.0)
+    out = dict([phase("alone", 0), phase("beside_copy", args.copy_workgroups), phase("beside_1wg_copy", 1)])
+    stop.set()
+    th.join(timeout=15)
+    log("smi: " + ", ".join(f"{k} {v['block_ms']:.3f} ms {v['gfx_mhz']} MHz {v['power_w']} W" for k, v in out.items()))
+    return out
 
 
 if __name__ == "__main__":
