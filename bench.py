@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--smi", action="store_true",
                     help="also sample GPU clock and power (amd-smi) while the block runs alone, beside the "
                          "copy and beside a one-workgroup copy")
+    ap.add_argument("--shape-study", action="store_true",
+                    help="also time the expert GEMMs under other row distributions with the same rows "
+                         "(balanced, dense, sparse/dense parts of the routed one) and hipBLASLt (torch) on "
+                         "contiguous operands of the same shapes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run the slice-copy kernel on BYTES bytes (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -275,11 +279,117 @@ def main():
         res["pipeline"] = measure_pipeline(layer, block, step, args, cfg, res["prefetch"])
     if not args.no_merge and cfg.n_prefetch > 0:
         res["merge_ablation"] = measure_merge(layer, block, cfg, b, stage_ms)
+    if args.shape_study:
+        res["shape_study"] = measure_shapes(layer, block, cfg, b)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def _median_ms(fn, reps=5, warm=2):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def measure_shapes(layer, block, cfg, b):
+    """Where the expert GEMMs' time goes, from the row distribution alone.
+
+    The same grouped FFN entry point runs on offsets other than the routed ones (every call keeps
+    rows == offsets[G], using the first rows of perm_src):
+      * routed:   the layer's own routing;
+      * balanced: every routed expert R/E rows, the shared expert T;
+      * dense:    k routed experts with T rows each plus the shared expert, so the rows are the
+                  routed ones' but the weights touched are few and reused from cache;
+      * split:    the routed counts cut at a row threshold into the sparse groups alone and the
+                  others alone (their times add up to the routed time when the two kinds do not
+                  overlap).
+    Reference (bf16 only): hipBLASLt through torch on contiguous operands of the balanced shapes --
+    a batched product over the E experts of R/E rows plus one product for the shared expert, for
+    GEMM1 ([rows, H] x [H, 2I]) and GEMM2 ([rows, I] x [I, H]); no pointer table, no SwiGLU.
+    """
+    import torch
+
+    from split_weight_expert_amd import api
+
+    G = cfg.E + cfg.shared
+    table = layer.table(1)
+    routed = np.diff(b.offsets.cpu().numpy()).astype(np.int64)
+    saved = b.offsets.clone()
+    fl1 = 4 * cfg.H * cfg.I
+
+    def run(counts):
+        counts = np.asarray(counts, dtype=np.int64)
+        offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(layer.device)
+        rows = int(counts.sum())
+        ps = b.perm_src[:rows]
+
+        def stage(s):
+            api.moe_grouped_ffn_tokens(s, table, G, offs, ps, b.x_tokens, b.x_q_scale, cfg.H, cfg.I, block.w_dtype,
+                                       b.y_perm, b.ws_ffn)
+        stage(1)
+        g1 = _median_ms(lambda: stage(1))
+        g2 = _median_ms(lambda: stage(2))   # reads the A that the last GEMM1 left in the workspace
+        return dict(rows=rows, groups=int((counts > 0).sum()), gemm1_ms=g1, gemm2_ms=g2,
+                    gemm1_tflops=fl1 * rows / g1 / 1e9, gemm2_tflops=fl1 / 2 * rows / g2 / 1e9)
+
+    out = {"routed": run(routed)}
+    if cfg.R % cfg.E == 0:
+        bal = np.full(G, cfg.R // cfg.E, dtype=np.int64)
+        bal[cfg.E:] = cfg.T
+        out["balanced"] = run(bal)
+    dense = np.zeros(G, dtype=np.int64)
+    dense[:cfg.k] = cfg.T
+    dense[cfg.E:] = cfg.T
+    out["dense"] = run(dense)
+    splits = []
+    for thr in (32, 64):
+        sp = np.where(routed <= thr, routed, 0)
+        sp[cfg.E:] = 0
+        if sp.sum() == 0:
+            continue
+        a, d = run(sp), run(routed - sp)
+        splits.append(dict(max_rows=thr, sparse=a, rest=d, sum_gemm1_ms=a["gemm1_ms"] + d["gemm1_ms"],
+                           sum_gemm2_ms=a["gemm2_ms"] + d["gemm2_ms"]))
+    out["split"] = splits
+    b.offsets.copy_(saved)
+
+    if cfg.dtype == "bf16" and cfg.R % cfg.E == 0:
+        n = cfg.R // cfg.E
+        dev, bf = layer.device, torch.bfloat16
+        ref = {}
+        for name, K, N in (("gemm1", cfg.H, 2 * cfg.I), ("gemm2", cfg.I, cfg.H)):
+            a = torch.randn(cfg.E, n, K, device=dev, dtype=bf)
+            w = (torch.randn(cfg.E, K, N, device=dev) / math.sqrt(K)).to(bf)   # contiguous [E, K, N]
+            o = torch.empty(cfg.E, n, N, device=dev, dtype=bf)
+            xs = torch.randn(cfg.T, K, device=dev, dtype=bf)
+            ws = (torch.randn(K, N, device=dev) / math.sqrt(K)).to(bf)
+            os_ = torch.empty(cfg.T, N, device=dev, dtype=bf)
+
+            def f():
+                torch.bmm(a, w, out=o)
+                torch.matmul(xs, ws, out=os_)
+            ms = _median_ms(f)
+            ms_dense = _median_ms(lambda: torch.matmul(xs, ws, out=os_))
+            rows = cfg.E * n + cfg.T
+            ref[name] = dict(ms=ms, tflops=2 * K * N * rows / ms / 1e9, dense_T_ms=ms_dense,
+                             dense_T_tflops=2 * K * N * cfg.T / ms_dense / 1e9)
+            del a, w, o, xs, ws, os_
+        torch.cuda.empty_cache()
+        out["hipblaslt_balanced"] = ref
+    return out
 
 
 def measure_merge(layer, block, cfg, b, stage_ms):

@@ -63,6 +63,8 @@ __device__ void plan_entry(const CopyArgs& a, int64_t P, int& src, int64_t& c) {
     }
 }
 
+constexpr int kCopyUnroll = 16;
+
 __global__ __launch_bounds__(256) void slice_copy_kernel(CopyArgs a) {
     __shared__ int s_src;
     __shared__ int64_t s_c;
@@ -85,15 +87,14 @@ __global__ __launch_bounds__(256) void slice_copy_kernel(CopyArgs a) {
         const v4u* f4 = reinterpret_cast<const v4u*>(from);
         v4u* t4 = reinterpret_cast<v4u*>(to);
         uint64_t i = threadIdx.x;
-        for (; i + 3 * 256 < nvec; i += 4 * 256) {
-            v4u v0 = __builtin_nontemporal_load(f4 + i);
-            v4u v1 = __builtin_nontemporal_load(f4 + i + 256);
-            v4u v2 = __builtin_nontemporal_load(f4 + i + 512);
-            v4u v3 = __builtin_nontemporal_load(f4 + i + 768);
-            __builtin_nontemporal_store(v0, t4 + i);
-            __builtin_nontemporal_store(v1, t4 + i + 256);
-            __builtin_nontemporal_store(v2, t4 + i + 512);
-            __builtin_nontemporal_store(v3, t4 + i + 768);
+        // kCopyUnroll loads per lane in flight (64 KB per workgroup): one workgroup then moves about
+        // as much as a CU can pull from HBM, so a few workgroups carry the whole copy
+        for (; i + (kCopyUnroll - 1) * 256 < nvec; i += kCopyUnroll * 256) {
+            v4u v[kCopyUnroll];
+#pragma unroll
+            for (int j = 0; j < kCopyUnroll; ++j) v[j] = __builtin_nontemporal_load(f4 + i + j * 256);
+#pragma unroll
+            for (int j = 0; j < kCopyUnroll; ++j) __builtin_nontemporal_store(v[j], t4 + i + j * 256);
         }
         for (; i < nvec; i += 256) __builtin_nontemporal_store(__builtin_nontemporal_load(f4 + i), t4 + i);
         for (uint64_t b = nvec * 16 + threadIdx.x; b < n; b += 256) to[b] = from[b];
