@@ -555,16 +555,17 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block):
         e1.record(cs)
         torch.cuda.synchronize()
         t_copy.append(e0.elapsed_time(e1))
-    # block and copy together: both streams start from the same point
+    # block and copy together: both streams start from the same point.  The block is enqueued first:
+    # the SDMA engine's host enqueue blocks for a while and must not delay the block's launch.
     t_blk, t_cp, t_tot = [], [], []
     for _ in range(reps):
         start = torch.cuda.Event(enable_timing=True)
         b_end = torch.cuda.Event(enable_timing=True)
         c_end = torch.cuda.Event(enable_timing=True)
         start.record(comp)
-        copy(wait=start, done=c_end)
         step()
         b_end.record(comp)
+        copy(wait=start, done=c_end)
         torch.cuda.synchronize()
         t_blk.append(start.elapsed_time(b_end))
         t_cp.append(start.elapsed_time(c_end))
