@@ -382,12 +382,13 @@ def test_combine_parity(dt, shared):
 def test_prefetch_copies_every_byte(engine):
     from split_weight_expert_amd import api
     rng = np.random.default_rng(engine)
-    sizes = [1_000_000, 3_333_344, 0, 2_097_152]
+    # an empty source, short last slices and an odd byte count (the copy kernel's vector tail and byte tail)
+    sizes = [1_000_000, 3_333_344, 0, 2_097_152, 777_777]
     chunk = 262_144
     srcs_np = [rng.integers(0, 256, size=n, dtype=np.uint8) for n in sizes]
     srcs = [torch.from_numpy(a).to(DEV) if len(a) else torch.empty(16, dtype=torch.uint8, device=DEV)
             for a in srcs_np]
-    offs = [0, 1_000_000, 4_333_344, 4_333_344]
+    offs = [0, 1_000_000, 4_333_344, 4_333_344, 6_430_496]
     total = offs[-1] + sizes[-1] + 64
     dst = torch.full((total,), 7, dtype=torch.uint8, device=DEV)
     cs = torch.cuda.Stream()
