@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--copy-workgroups", type=int, default=48)
     ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy", "sdma"])
     ap.add_argument("--chunk-mib", type=float, default=0, help="prefetch slice size in MiB (default: the workload's 4)")
+    ap.add_argument("--copy-streams", type=int, default=1,
+                    help="deal the prefetch's source regions round-robin over this many copy streams (the kernel "
+                         "engine splits --copy-workgroups between them)")
     ap.add_argument("--smi", action="store_true",
                     help="also sample GPU clock and power (amd-smi) while the block runs alone, beside the "
                          "copy and beside a one-workgroup copy")
@@ -536,12 +539,24 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block):
     nbytes = sum(s[2] for s in layer.sources)
     cs = torch.cuda.Stream()
     comp = torch.cuda.current_stream()
+    n_cs = max(1, min(args.copy_streams, len(layer.sources)))
+    extra = [torch.cuda.Stream() for _ in range(n_cs - 1)]
 
     chunk = int(args.chunk_mib * (1 << 20)) if args.chunk_mib else cfg.chunk_bytes
 
     def copy(wait=None, done=None):
-        api.prefetch_chunks(dst, layer.sources, chunk, engine=engine, max_workgroups=args.copy_workgroups,
-                            copy_stream=cs, wait_event=wait, done_event=done)
+        # stream i copies source regions i, i + n, ...; the other streams join cs before `done`
+        for st in extra:
+            st.wait_stream(cs)
+        for i, st in enumerate([cs] + extra):
+            api.prefetch_chunks(dst, layer.sources[i::n_cs], chunk, engine=engine,
+                                max_workgroups=max(1, args.copy_workgroups // n_cs), copy_stream=st, wait_event=wait,
+                                done_event=done if n_cs == 1 else None)
+        if n_cs > 1:
+            for st in extra:
+                cs.wait_stream(st)
+            if done is not None:
+                done.record(cs)
 
     reps = max(3, min(args.steps, 10))
     # copy alone
@@ -574,7 +589,7 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block):
     per = cfg.n_prefetch // cfg.n_sources
     ok = bool(torch.equal(layer.store.record(2, per + 1), layer.src_store.record(1, 1)))
     c_alone = float(np.median(t_copy))
-    return dict(engine=args.copy_engine, workgroups=args.copy_workgroups, bytes=nbytes, chunk_bytes=chunk,
+    return dict(engine=args.copy_engine, workgroups=args.copy_workgroups, streams=n_cs, bytes=nbytes, chunk_bytes=chunk,
                 n_chunks=len(api.prefetch_plan(layer.sources, chunk)),
                 copy_ms=c_alone, copy_gbps=nbytes / c_alone / 1e6,
                 block_ms_alone=ms_block, block_ms_with_copy=float(np.median(t_blk)),
