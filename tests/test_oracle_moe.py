@@ -269,6 +269,25 @@ def test_bf16_policy_rounds_outputs_to_bf16_values():
     assert rel.max() < 2e-2 and rel.mean() < 2e-3                      # rounding error only
 
 
+def test_bf16_policy_rounds_the_intermediate_before_the_down_projection():
+    """Rounding point of the bf16 policy: A = silu(X Wg^T) * (X Wu^T) is rounded to bf16 (torch's own
+    conversion) before it meets Wd, and Y is the bf16 rounding of that A times Wd^T."""
+    cfg = shrink(synth.get_config("decode64_bf16"), T=8, H=256, I=128, E=8, k=2)
+    x, wr, b, ex = tiny_layer(cfg)
+    wg, wu, wd = moe.prepare_weights(*ex[3], "bf16")
+    X = moe.prepare_tokens(x, "bf16")
+    parts = moe.expert_ffn_parts(X, wg, wu, wd, "bf16")
+    f = torch.nn.functional
+    Xt = torch.from_numpy(np.asarray(X, np.float64))
+    a = f.silu(f.linear(Xt, torch.from_numpy(wg))) * f.linear(Xt, torch.from_numpy(wu))
+    a_bf16 = a.to(torch.bfloat16).to(torch.float64)
+    np.testing.assert_array_equal(parts["A"], a_bf16.numpy())
+    y = f.linear(a_bf16, torch.from_numpy(wd)).to(torch.bfloat16).to(torch.float64).numpy()
+    ulp = np.abs(y) * 2.0 ** -7
+    assert np.all(np.abs(parts["Y"] - y) <= ulp)          # equal up to one bf16 step (fp64 sum order)
+    assert np.mean(parts["Y"] == y) > 0.99
+
+
 # ----------------------------------------------------------------------------------------------
 # fp8 quantisation
 
