@@ -386,9 +386,12 @@ struct FragCfg {
     static constexpr int BBYTES = 4 * BI * 1024;
     // fp8: a step's slot also holds the row scales of its K block.  Each wave loads those of RW rows
     // with one 64-lane DMA instruction into a 64-float slice of its own (lanes past RW repeat the
-    // last row), so row R's scale sits at float (R / RW) * 64 + R % RW.
+    // last row), so row R's scale sits at float (R / RW) * SSTRIDE + R % RW.  Slices are SSTRIDE = 80
+    // floats apart: the 32 rows one read serves span two slices, and the 16-float shift puts them
+    // on different LDS banks (at 64 floats apart the two halves collide).
     static constexpr int RW = BM / NW;
-    static constexpr int STAGE = ABYTES + BBYTES + (FP8 ? NW * 64 * 4 : 0);
+    static constexpr int SSTRIDE = 80;                        // floats between waves' scale slices
+    static constexpr int STAGE = ABYTES + BBYTES + (FP8 ? NW * SSTRIDE * 4 : 0);
     // fp8, outside the ring: the weight block scales of each wave's n-blocks (K / 128 <= 64), read
     // once per tile
     static constexpr int BSC = FP8 ? NW * NJ * 64 : 0;        // floats
@@ -474,7 +477,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     [[maybe_unused]] auto scale_dma = [&](int kt, uint8_t* st) {
-        dma4(reinterpret_cast<const uint8_t*>(gs + kt), st + ABYTES + BBYTES + wave * 256);
+        dma4(reinterpret_cast<const uint8_t*>(gs + kt), st + ABYTES + BBYTES + wave * C::SSTRIDE * 4);
     };
     auto issue = [&](int kt, int buf) {
         uint8_t* st = smem + buf * STAGE;
@@ -543,7 +546,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                                      (int)up[2], (int)up[3]};
                 }
                 const int R = rbase + i * 32 + l32;
-                sa[i] = sa_lds[(R / C::RW) * 64 + R % C::RW];
+                sa[i] = sa_lds[(R / C::RW) * C::SSTRIDE + R % C::RW];
             }
             // The fold of an output block needs its MFMAs' result, so block b's fold is issued after
             // block b+1's MFMAs: the VALU folds while the matrix core multiplies.
