@@ -1,6 +1,12 @@
-// Router: logits = x * W_r^T + b (gemm.hip), then per token the top-k experts and
-// their renormalised softmax weights.  The pages give no gate formula; the gate
-// here is softmax top-k with the weights renormalised over the chosen k.
+// Router: logits = x * W_r^T + b, then per token the top-k experts and their
+// renormalised softmax weights.  The pages give no gate formula; the gate here is
+// softmax top-k with the weights renormalised over the chosen k.
+//
+// Logits: prefill batches use the tiled MFMA kernel of gemm.hip.  A decode-sized
+// batch (T <= 256 tokens, bf16) would give that kernel only a few workgroups, each
+// walking all of K, so it uses router_splitk_kernel here: 32 x 32 tiles, the K range
+// split over the workgroup's 8 waves, partial tiles summed through LDS in wave order
+// (a fixed order, so the logits are reproducible bit for bit).
 //
 // Top-k: one wavefront per token.  Lane l holds logits l, l+64, l+128, ...;
 // k rounds of (lane-local best, then a 64-lane butterfly max on (value desc,
@@ -14,6 +20,64 @@ int router_gemm(const void* x, const void* w, int dtype, const float* bias, int6
                 hipStream_t st);
 
 namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kSplitMaxT = 256;    // batches up to this many tokens take the split-K router
+constexpr int kSplitWaves = 8;
+
+// logits[T, E] for one 32-token x 32-expert tile.  Wave w multiplies K columns [w H/8, (w+1) H/8)
+// with v_mfma_f32_32x32x16_bf16, operands loaded straight from global memory (lane l: row l % 32,
+// 8 columns at 8 (l / 32)); rows past T or E are clamped for loads and skipped for stores.
+__global__ __launch_bounds__(kSplitWaves * 64) void router_splitk_kernel(const uint16_t* __restrict__ x,
+                                                                        const uint16_t* __restrict__ wr,
+                                                                        const float* __restrict__ bias, int T,
+                                                                        int H, int E, float* __restrict__ logits) {
+    __shared__ float part[kSplitWaves][64][17];   // 17: consecutive lanes fall on different banks
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, hi = lane >> 5;
+    const int m0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
+    const uint16_t* arow = x + (size_t)min(m0 + l32, T - 1) * H + hi * 8;
+    const uint16_t* brow = wr + (size_t)min(n0 + l32, E - 1) * H + hi * 8;
+    const int kw = H / kSplitWaves;
+    const int kb = wave * kw, ke = kb + kw;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    constexpr int U = 8;                           // K16 steps per batch of loads
+    int k = kb;
+    for (; k + 16 * U <= ke; k += 16 * U) {
+        bf16x8 a[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            a[u] = *reinterpret_cast<const bf16x8*>(arow + k + 16 * u);
+            b[u] = *reinterpret_cast<const bf16x8*>(brow + k + 16 * u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u], acc, 0, 0, 0);
+    }
+    for (; k < ke; k += 16) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + k);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(brow + k);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+    // element r of lane (l32, hi): token m0 + 8 (r / 4) + 4 hi + r % 4, expert n0 + l32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[wave][lane][r] = acc[r];
+    __syncthreads();
+    if (wave == 0) {
+        const int e = n0 + l32;
+        const float b = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = part[0][lane][r];
+#pragma unroll
+            for (int w = 1; w < kSplitWaves; ++w) s += part[w][lane][r];
+            const int t = m0 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            if (t < T && e < E) logits[(size_t)t * E + e] = s + b;
+        }
+    }
+}
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
@@ -98,8 +162,15 @@ extern "C" int dwdp_route_topk(const void* x, const void* w_router, int in_dtype
     DWDP_REQUIRE(x && w_router && logits_out && topk_idx && topk_w, "null pointer argument");
     DWDP_REQUIRE(aligned16(x) && aligned16(w_router), "x and w_router must be 16-byte aligned");
     hipStream_t st = as_stream(stream);
-    int rc = router_gemm(x, w_router, in_dtype, bias, T, H, E, logits_out, st);
-    if (rc != DWDP_OK) return rc;
+    if (in_dtype == DWDP_BF16 && T <= kSplitMaxT && H % (kSplitWaves * 16) == 0) {
+        hipLaunchKernelGGL(router_splitk_kernel, dim3((unsigned)((T + 31) / 32), (unsigned)((E + 31) / 32)),
+                           dim3(kSplitWaves * 64), 0, st, static_cast<const uint16_t*>(x),
+                           static_cast<const uint16_t*>(w_router), bias, (int)T, H, E, logits_out);
+        DWDP_LAUNCHED();
+    } else {
+        int rc = router_gemm(x, w_router, in_dtype, bias, T, H, E, logits_out, st);
+        if (rc != DWDP_OK) return rc;
+    }
     hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, logits_out, T, E, k, topk_idx,
                        topk_w);
     DWDP_LAUNCHED();
