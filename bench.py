@@ -252,6 +252,7 @@ def main():
     ms_step = wall / args.steps * 1e3
     names = ["route", "permute", "gemm1_swiglu", "gemm2", "combine"]
     stage_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    step_ev_ms = [e[0].elapsed_time(e[5]) for e in evs]      # each step between its first and last event
     log(f"step {ms_step:.3f} ms; stages " + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
 
     counts = np.diff(b.offsets.cpu().numpy())
@@ -272,7 +273,10 @@ def main():
                tflops_ffn=flops_ffn / ((stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) / 1e3) / 1e12,
                frac_peak_ffn=flops_ffn / ((stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) / 1e3) / peak,
                weight_gbps_ffn=touched * wbytes / ((stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) / 1e3) / 1e9,
-               experts_touched=touched, rows=rows, stage_ms=stage_ms, roofline=res_roof)
+               experts_touched=touched, rows=rows, stage_ms=stage_ms,
+               step_ms_events=dict(p10=float(np.percentile(step_ev_ms, 10)), median=float(np.median(step_ev_ms)),
+                                   p90=float(np.percentile(step_ev_ms, 90))),
+               roofline=res_roof)
 
     if want_prefetch:
         res["prefetch"] = measure_prefetch(layer, block, step, args, cfg, ms_step)
@@ -562,6 +566,11 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block):
     # copy alone
     copy()
     torch.cuda.synchronize()
+    # host time to enqueue the whole plan (one launch for the kernel engine, one call per slice otherwise)
+    h0 = time.perf_counter()
+    copy()
+    host_s = time.perf_counter() - h0
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_copy = []
     for _ in range(reps):
@@ -591,6 +600,7 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block):
     c_alone = float(np.median(t_copy))
     return dict(engine=args.copy_engine, workgroups=args.copy_workgroups, streams=n_cs, bytes=nbytes, chunk_bytes=chunk,
                 n_chunks=len(api.prefetch_plan(layer.sources, chunk)),
+                host_enqueue_us_per_chunk=host_s * 1e6 / max(1, len(api.prefetch_plan(layer.sources, chunk))),
                 copy_ms=c_alone, copy_gbps=nbytes / c_alone / 1e6,
                 block_ms_alone=ms_block, block_ms_with_copy=float(np.median(t_blk)),
                 copy_ms_with_block=float(np.median(t_cp)), layer_ms_overlapped=float(np.median(t_tot)),
