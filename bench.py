@@ -257,6 +257,11 @@ def main():
 
     counts = np.diff(b.offsets.cpu().numpy())
     rows = int(counts.sum())
+    routed = np.sort(counts[:cfg.E].astype(np.float64))
+    # Gini coefficient of the routed experts' row counts (0: every expert the same load)
+    gini = float((2 * np.arange(1, cfg.E + 1) - cfg.E - 1) @ routed / (cfg.E * routed.sum())) if routed.sum() else 0.0
+    load = dict(max_rows=int(routed[-1]), median_rows=float(np.median(routed)), min_rows=int(routed[0]),
+                empty_experts=int((routed == 0).sum()), gini=gini)
     touched = int((counts[:cfg.E] > 0).sum()) + cfg.shared
     flops_ffn = 6 * cfg.H * cfg.I * rows
     flops_total = flops_ffn + 2 * cfg.T * cfg.H * cfg.E
@@ -273,7 +278,7 @@ def main():
                tflops_ffn=flops_ffn / ((stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) / 1e3) / 1e12,
                frac_peak_ffn=flops_ffn / ((stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) / 1e3) / peak,
                weight_gbps_ffn=touched * wbytes / ((stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) / 1e3) / 1e9,
-               experts_touched=touched, rows=rows, stage_ms=stage_ms,
+               experts_touched=touched, rows=rows, expert_load=load, stage_ms=stage_ms,
                step_ms_events=dict(p10=float(np.percentile(step_ev_ms, 10)), median=float(np.median(step_ev_ms)),
                                    p90=float(np.percentile(step_ev_ms, 90))),
                roofline=res_roof)
