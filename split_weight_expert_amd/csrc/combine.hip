@@ -1,7 +1,9 @@
 // Weighted unpermute: y[t] = sum_j w[t,j] * y_perm[inv_perm[t,j]] (+ y_perm[T*k + t]),
 // summed in fp32 in slot order, then the shared row, rounded once.  One
 // workgroup per token; each thread owns 8 consecutive columns (16-byte bf16
-// vectors).  Entries with inv_perm < 0 (dropped assignments) contribute nothing.
+// vectors) and issues the loads of up to 8 source rows together before summing
+// them in slot order.  Entries with inv_perm < 0 (dropped assignments) contribute
+// nothing.
 #include "common.h"
 #include "internal.h"
 
@@ -26,28 +28,48 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict_
     __syncthreads();
     const int64_t shared_row = T * k + t;
     const int nvec = H / 8;
+    const int nsrc = k + (shared ? 1 : 0);                // source rows: the k slots, then the shared row
+    constexpr int B = 8;                                  // rows whose loads are in flight together
     for (int c = threadIdx.x; c < nvec; c += 256) {
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        auto add_row = [&](int64_t row, float wt) {
-            if (BF16) {
-                const uint4 raw = *reinterpret_cast<const uint4*>(y_perm + (row * H + c * 8) * 2);
-                const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+        for (int j0 = 0; j0 < nsrc; j0 += B) {
+            // all loads of the batch first (a dropped slot loads row 0 and is skipped below) ...
+            uint4 raw[BF16 ? B : 2 * B];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] += wt * bf16_to_f32((uint16_t)(wd[i] & 0xffffu));
-                    acc[2 * i + 1] += wt * bf16_to_f32((uint16_t)(wd[i] >> 16));
+            for (int u = 0; u < B; ++u) {
+                const int j = j0 + u;
+                if (j < nsrc) {
+                    const int64_t row = j < k ? (s_row[j] >= 0 ? s_row[j] : 0) : shared_row;
+                    if (BF16) {
+                        raw[u] = *reinterpret_cast<const uint4*>(y_perm + (row * H + c * 8) * 2);
+                    } else {
+                        const uint4* q = reinterpret_cast<const uint4*>(y_perm + (row * H + c * 8) * 4);
+                        raw[2 * u] = q[0];
+                        raw[2 * u + 1] = q[1];
+                    }
                 }
-            } else {
-                const float4* p = reinterpret_cast<const float4*>(y_perm + (row * H + c * 8) * 4);
-                const float4 a = p[0], b = p[1];
-                const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += wt * v[i];
             }
-        };
-        for (int j = 0; j < k; ++j)
-            if (s_row[j] >= 0) add_row(s_row[j], s_w[j]);
-        if (shared) add_row(shared_row, 1.0f);
+            // ... then the sums, in slot order
+#pragma unroll
+            for (int u = 0; u < B; ++u) {
+                const int j = j0 + u;
+                if (j >= nsrc || (j < k && s_row[j] < 0)) continue;
+                const float wt = j < k ? s_w[j] : 1.0f;
+                if (BF16) {
+                    const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[2 * i] += wt * bf16_to_f32((uint16_t)(wd[i] & 0xffffu));
+                        acc[2 * i + 1] += wt * bf16_to_f32((uint16_t)(wd[i] >> 16));
+                    }
+                } else {
+                    const uint32_t wd[8] = {raw[2 * u].x, raw[2 * u].y, raw[2 * u].z, raw[2 * u].w,
+                                            raw[2 * u + 1].x, raw[2 * u + 1].y, raw[2 * u + 1].z, raw[2 * u + 1].w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] += wt * __uint_as_float(wd[i]);
+                }
+            }
+        }
         if (BF16) {
             uint32_t o[4];
 #pragma unroll
