@@ -256,13 +256,55 @@ def prefetch_last_slice_full():
     p.chunk_plan = plan
 
 
+def fp8_a_not_requantised():
+    m = _moe()
+
+    def parts(X, wg, wu, wd, precision):
+        X = np.asarray(X, np.float64)
+        A = m.silu(X @ wg.T) * (X @ wu.T)
+        if precision == "bf16":
+            A = m.bf16_round(A)
+        Y = A @ wd.T
+        if precision in ("bf16", "fp8"):
+            Y = m.bf16_round(Y)
+        return dict(A=A, A_codes=None, A_scales=None, Y=Y)
+    m.expert_ffn_parts = parts
+
+
+def fp8_scale_divisor_447():
+    def scale(amax32):
+        s = (amax32.astype(np.float32) / np.float32(447.0)).astype(np.float32)
+        return np.where(amax32 == 0, np.float32(1.0), s).astype(np.float32)
+    _moe()._fp32_scale = scale
+
+
+def fp8_output_not_rounded():
+    m = _moe()
+
+    def parts(X, wg, wu, wd, precision):
+        X = np.asarray(X, np.float64)
+        A = m.silu(X @ wg.T) * (X @ wu.T)
+        codes = scales = None
+        if precision == "bf16":
+            A = m.bf16_round(A)
+        elif precision == "fp8":
+            codes, scales = m.quantize_groups(A.astype(np.float32))
+            A = m.dequant_groups(codes, scales)
+        Y = A @ wd.T
+        if precision == "bf16":
+            Y = m.bf16_round(Y)
+        return dict(A=A, A_codes=codes, A_scales=scales, Y=Y)
+    m.expert_ffn_parts = parts
+
+
 MUTANTS = {f.__name__: f for f in [
     silu_sign, swiglu_gate_up_swapped, swiglu_up_dropped, bf16_intermediate_not_rounded,
     combine_shared_dropped, combine_unweighted, combine_weights_reversed,
     topk_ties_to_higher_index, topk_smallest, gate_not_renormalised, router_bias_sign, router_bias_dropped,
     permute_reversed_within_expert, permute_shared_rows_first, permute_inverse_not_inverted,
     bf16_truncates, e4m3_ties_away_from_zero, e4m3_overflow_to_nan, fp8_scale_uses_fnuz_max,
-    fp8_block_amax_wrong_axes, prefetch_source_major, prefetch_last_slice_full,
+    fp8_block_amax_wrong_axes, fp8_a_not_requantised, fp8_scale_divisor_447, fp8_output_not_rounded,
+    prefetch_source_major, prefetch_last_slice_full,
 ]}
 
 

@@ -3,7 +3,7 @@ import os
 
 import numpy as np
 
-from oracle import codecs
+from oracle import codecs, moe
 from oracle.prefetch import chunk_plan
 
 HERE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -34,3 +34,34 @@ def test_fp8_overlap_slice_plan():
     assert len(plan) == int(rows["n_slices"][0])
     assert [tuple(p) for p in plan[:len(firsts)]] == firsts
     assert [tuple(p) for p in plan[-len(lasts):]] == lasts
+
+
+def _group(amax, value=None):
+    """One 128-wide group: amax in column 0, `value` (if any) in column 1, zeros elsewhere."""
+    g = np.zeros((1, 128), np.float32)
+    g[0, 0] = amax
+    if value is not None:
+        g[0, 1] = value
+    return g
+
+
+def test_fp8_group_scales_and_codes():
+    rows = lines("fp8_group_scales.txt")
+    scales = [(float(a), int(b, 16)) for kind, a, b in (r for r in rows if r[0] == "scale")]
+    codes = [(float(a), float(v), int(c, 16)) for kind, a, v, c in (r for r in rows if r[0] == "code")]
+    assert scales and codes
+    for amax, bits in scales:
+        _, s = moe.quantize_groups(_group(amax))
+        assert s.dtype == np.float32 and int(s.view(np.uint32)[0, 0]) == bits, (amax, hex(int(s.view(np.uint32)[0, 0])))
+        blk = np.zeros((128, 128), np.float32)
+        blk[5, 7] = amax
+        _, sb = moe.quantize_blocks(blk)
+        assert int(sb.view(np.uint32)[0, 0]) == bits, amax
+    for amax, v, code in codes:
+        q, _ = moe.quantize_groups(_group(amax, v))
+        assert int(q[0, 1]) == code, (amax, v, hex(int(q[0, 1])))
+        blk = np.zeros((128, 128), np.float32)
+        blk[0, 0] = amax
+        blk[100, 3] = v
+        qb, _ = moe.quantize_blocks(blk)
+        assert int(qb[100, 3]) == code, (amax, v)

@@ -341,3 +341,44 @@ def test_fp8_policy_dense_equals_sparse():
             Y = moe.expert_ffn(xq, *moe.prepare_weights(*ex[e], "fp8"), "fp8")
             y[t] += out["w"][t, j] * Y[t]
     np.testing.assert_allclose(out["y"], moe.bf16_round(y), rtol=0, atol=1e-12 + 2**-7 * np.abs(y).max())
+
+
+def test_fp8_expert_against_torch_float8():
+    """Tokens through one fp8 expert with H = I = 128, written out with torch's float8_e4m3fn.
+
+    At H = I = 128 every weight matrix is a single 128x128 block and every token row (and every
+    row of the intermediate A) a single 128-wide group, so each scale is one amax / 448 (fp32).
+    The expert is spelled out from that definition: tokens and weights quantised and dequantised
+    with torch's E4M3 conversion, G and U in float64, A = silu(G) * U re-quantised per row before
+    the down projection, Y rounded to bf16 with torch's conversion.  This pins the re-quantisation
+    of A, the 448 in the scale and the bf16 rounding of the expert output (reading 10 of the fp8
+    policy; the pages' own format is NVFP4, DWDP paper summary Section 5.1).
+    """
+    rng = np.random.default_rng(21)
+    x = rng.normal(0, 1, size=(8, 128)).astype(np.float32)
+    x[3] *= 40.0                                          # a token with large values
+    wg, wu, wd = (rng.normal(0, 128 ** -0.5, size=(128, 128)).astype(np.float32) for _ in range(3))
+
+    def q(v, rows):
+        """Quantise v per row (rows=True) or as one block; returns (dequantised fp64, codes, scales)."""
+        v = torch.from_numpy(np.ascontiguousarray(v, np.float32))
+        amax = v.abs().amax(dim=1, keepdim=True) if rows else v.abs().max().reshape(1, 1)
+        s = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)          # fp32 division
+        c = (v / s).to(torch.float8_e4m3fn)
+        return c.to(torch.float64) * s.to(torch.float64), c.view(torch.uint8).numpy(), s.numpy()
+
+    xd = q(x, True)[0]
+    wgd, wud, wdd = (q(w, False)[0] for w in (wg, wu, wd))
+    f = torch.nn.functional
+    a = f.silu(xd @ wgd.T) * (xd @ wud.T)
+    ad, a_codes, a_scales = q(a.to(torch.float32).numpy(), True)
+    y = (ad @ wdd.T).to(torch.bfloat16).to(torch.float64).numpy()
+
+    parts = moe.expert_ffn_parts(moe.prepare_tokens(x, "fp8"), *moe.prepare_weights(wg, wu, wd, "fp8"), "fp8")
+    assert parts["A_codes"] is not None
+    np.testing.assert_array_equal(parts["A_codes"], a_codes)
+    np.testing.assert_array_equal(parts["A_scales"], a_scales[:, :1].reshape(-1, 1))
+    np.testing.assert_array_equal(parts["A"], ad.numpy())
+    ulp = np.abs(y) * 2.0 ** -7
+    assert np.all(np.abs(parts["Y"] - y) <= ulp)          # equal up to one bf16 step (fp64 sum order)
+    assert np.mean(parts["Y"] == y) > 0.99
