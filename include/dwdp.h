@@ -30,8 +30,9 @@
  *   - T == 0 (no tokens) is a valid no-op.
  *   - Results are bitwise deterministic for identical inputs and do not depend
  *     on which buffer or slot an expert's weights sit in.
- *   - Device-side index values outside their range (a topk_idx entry outside
- *     [0, E)) are not diagnosed; kernels stay in bounds and drop such entries.
+ *   - Device-side index values outside their range are not diagnosed (that would
+ *     need a host synchronisation); kernels stay in bounds and the results stay
+ *     defined.  A topk_idx entry outside [0, E) is dropped: see dwdp_permute.
  *
  * Layouts (row-major, C order)
  *   x          [T, H]            tokens, bf16 (f32 for the f32 path)
@@ -126,6 +127,11 @@ int dwdp_route_topk(const void* x, const void* w_router, int in_dtype, const flo
                     float* logits_out, int32_t* topk_idx, float* topk_w, void* stream);
 
 /* Permutation by expert (counting sort, stable in t*k+j) and row gather.
+ * The pages give no permutation (DWDP paper summary §2 only says that each rank
+ * runs its own MoE block on its own batch); the reading taken is the textbook
+ * one: experts in ascending order, inside an expert the assignments in
+ * ascending flattened index t*k+j, then the shared expert's T rows in token
+ * order.  The library builds it without atomics, so it is bitwise reproducible.
  *   topk_idx [T,k] int32.  shared in {0,1}.
  *   x [T,H] of x_dtype (F32 or BF16).  act_dtype == x_dtype copies rows bitwise;
  *   act_dtype == DWDP_FP8_E4M3 (x_dtype BF16, H % 128 == 0) quantises each row
@@ -134,6 +140,12 @@ int dwdp_route_topk(const void* x, const void* w_router, int in_dtype, const flo
  *   codes (uint8) and x_perm_scale [rows, H/128] the scales.
  *   Outputs: x_perm [rows,H], offsets [E+shared+1], perm_src [rows] (source token
  *   of each row), inv_perm [T,k] (row of each (t,j)).
+ *   Dropped entries: a topk_idx entry outside [0, E) is counted in no expert and
+ *   gets inv_perm = -1 (dwdp_combine skips it).  offsets[E] is T*k in every case,
+ *   so with D dropped entries the last D rows of the routed region, [T*k-D, T*k),
+ *   close the last routed group (expert E-1's range holds D more rows than its
+ *   count); their perm_src is 0, the grouped FFN computes them from token 0 and
+ *   nothing reads their output.  With valid indices (dwdp_route_topk's) D = 0.
  *   x_perm == NULL computes only offsets, perm_src and inv_perm (x, x_perm_scale
  *   are then not read): the caller feeds the tokens to
  *   dwdp_moe_grouped_ffn_tokens, which gathers the rows itself.
@@ -163,7 +175,8 @@ int dwdp_quantize_tokens_fp8(const void* x, int64_t T, int H, void* q, float* q_
  *     block and scaled by (row scale * block scale); A quantised per row and
  *     128-column group like x; y_perm bf16.
  *   rows must equal offsets[n_groups] (not checked on the device).  H % 256 == 0,
- *   I % 128 == 0 (BF16/FP8); H % 4, I % 4 == 0 (F32).  offsets is read on the
+ *   I % 128 == 0 (BF16/FP8; FP8 also H, I <= 8192); H % 64 == 0, I % 32 == 0
+ *   (F32).  Other shapes return DWDP_ERR_INVALID_ARG.  offsets is read on the
  *   device only; no host synchronisation happens.
  *   ws: dwdp_workspace_bytes(DWDP_OP_GROUPED_FFN, ...) bytes.  After GEMM1 it
  *     begins with A [rows, I] row-major in the activation type (fp32, bf16, or
@@ -196,7 +209,12 @@ int dwdp_moe_grouped_ffn_tokens(int stage, const dwdp_expert_ptrs* table, int n_
 
 /* Combine: y[t] = sum_{j<k} topk_w[t,j] * y_perm[inv_perm[t,j]] (+ y_perm[T*k + t]
  * when shared), summed in fp32 in slot order then the shared row, rounded once
- * to out_dtype.  y_perm is fp32 for out_dtype F32, bf16 otherwise. */
+ * to out_dtype.  y_perm is fp32 for out_dtype F32, bf16 otherwise.  The pages
+ * give no combine formula (DWDP paper summary §2: the rank runs an ordinary MoE
+ * block); this weighted sum with the shared expert added at weight 1 is the
+ * reading taken, with the summation order fixed so that the result is bitwise
+ * reproducible.  Slots with inv_perm < 0 or >= T*k + shared*T contribute nothing.
+ *   T >= 0, 1 <= k <= 64, H % 8 == 0; y_perm and y 16-byte aligned; y [T,H]. */
 int dwdp_combine(const void* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T, int k,
                  int shared, int H, int out_dtype, void* y, void* stream);
 

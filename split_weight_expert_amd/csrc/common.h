@@ -1,5 +1,5 @@
-// Internal helpers shared by the library's translation units: error state,
-// argument checks, and the device-side number conversions (bf16, E4M3).
+// Device-side helpers shared by the library's HIP translation units: HIP error checks and the
+// number conversions (bf16, E4M3).  The host-only helpers are in errors.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,27 +7,9 @@
 #include <stddef.h>
 #include <string>
 
-#include "../../include/dwdp.h"
+#include "errors.h"
 
 namespace dwdp {
-
-// ---------------------------------------------------------------- host: errors
-void set_error(const std::string& msg);
-void clear_error();
-
-struct Fail {
-    int code;
-};
-
-inline int fail(int code, const std::string& msg) {
-    set_error(msg);
-    return code;
-}
-
-#define DWDP_REQUIRE(cond, msg)                                                       \
-    do {                                                                              \
-        if (!(cond)) return ::dwdp::fail(DWDP_ERR_INVALID_ARG, std::string(__func__) + ": " + (msg)); \
-    } while (0)
 
 #define DWDP_HIP(call)                                                                \
     do {                                                                              \
@@ -43,12 +25,7 @@ inline int fail(int code, const std::string& msg) {
             return ::dwdp::fail(DWDP_ERR_HIP, std::string(__func__) + ": launch: " + hipGetErrorString(e_)); \
     } while (0)
 
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
-
-constexpr int kFp8Group = 128;     // activation group width and weight block edge
-constexpr int kNumXcd = 8;         // MI355X: 8 accelerator complex dies, 32 CUs each
 
 // ------------------------------------------------------------ device: numbers
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

@@ -46,6 +46,7 @@ struct MTile {
     int32_t mc;   // the group's m-tile count
     int32_t pad;
 };
+static_assert(sizeof(MTile) == kMTileBytes, "the workspace layout sizes the m-tile tables");
 
 struct GemmParams {
     const uint8_t* a;               // activation rows [rows, K]
@@ -1021,7 +1022,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 constexpr int kBnDma = 256;
 constexpr int kBmF32 = 64, kBnF32 = 64;
 constexpr int kBmRouter = 64, kBnRouter = 64;
-constexpr int kBmMin = 32;
 
 int choose_bm(int dtype, int64_t rows, int groups) {
     if (dtype == DWDP_F32) return kBmF32;
@@ -1030,33 +1030,6 @@ int choose_bm(int dtype, int64_t rows, int groups) {
     // fp8 stays at 128 rows: a 256-row tile only fits the LDS ring with 64-wide K steps, which folds
     // every partial sum twice per scale block (measured 11.7 vs 9.6 ms for GEMM1 at 16K tokens)
     return dtype == DWDP_FP8_E4M3 && bm > 128 ? 128 : bm;
-}
-
-size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
-
-struct FfnWs {
-    size_t a, a_scale, pre, mt, mt_by_size, total;
-};
-
-// Workspace: A [rows, I] (+ fp8 scales), the m-tile prefix [G+1] and the m-tile table, sized for
-// the smallest BM so that any choice fits.
-FfnWs ffn_ws_layout(int64_t rows, int groups, int I, int dtype) {
-    FfnWs w{};
-    const size_t ea = dtype == DWDP_F32 ? 4 : dtype == DWDP_BF16 ? 2 : 1;
-    const int64_t maxm = (rows + kBmMin - 1) / kBmMin + groups;
-    size_t off = 0;
-    w.a = off;
-    off += a256((size_t)rows * I * ea);
-    w.a_scale = off;
-    if (dtype == DWDP_FP8_E4M3) off += a256((size_t)rows * (I / kFp8Group) * 4);
-    w.pre = off;
-    off += a256((size_t)(groups + 1) * 4);
-    w.mt = off;
-    off += a256((size_t)maxm * sizeof(MTile));
-    w.mt_by_size = off;
-    off += a256((size_t)maxm * sizeof(MTile));
-    w.total = off;
-    return w;
 }
 
 template <int BM>
@@ -1106,12 +1079,6 @@ void launch_ffn(bool g1, bool g2, bool fp8_path, const int32_t* offsets, int G, 
 }
 
 }  // namespace
-
-size_t ffn_ws_bytes(int64_t rows, int groups, int H, int I, int dtype) {
-    (void)H;
-    if (dtype != DWDP_F32 && dtype != DWDP_BF16 && dtype != DWDP_FP8_E4M3) return 0;
-    return ffn_ws_layout(rows, groups, I, dtype).total;
-}
 
 // Router GEMM: logits [T, E] = x [T, H] * w_router^T + bias.
 int router_gemm(const void* x, const void* w, int dtype, const float* bias, int64_t T, int H, int E, float* logits,

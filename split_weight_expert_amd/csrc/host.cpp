@@ -6,7 +6,7 @@
 #include <string>
 #include <vector>
 
-#include "common.h"
+#include "errors.h"
 #include "internal.h"
 
 namespace dwdp {
@@ -46,13 +46,46 @@ void record_layout(int H, int I, int w_dtype, size_t* w2, size_t* s13, size_t* s
     *total = end;
 }
 
+FfnWs ffn_ws_layout(int64_t rows, int groups, int I, int dtype) {
+    FfnWs w{};
+    const size_t ea = elem_bytes(dtype);
+    const int64_t maxm = (rows + kBmMin - 1) / kBmMin + groups;
+    size_t off = 0;
+    w.a = off;
+    off += align256((size_t)rows * I * ea);
+    w.a_scale = off;
+    if (dtype == DWDP_FP8_E4M3) off += align256((size_t)rows * (I / kFp8Group) * 4);
+    w.pre = off;
+    off += align256((size_t)(groups + 1) * 4);
+    w.mt = off;
+    off += align256((size_t)maxm * kMTileBytes);
+    w.mt_by_size = off;
+    off += align256((size_t)maxm * kMTileBytes);
+    w.total = off;
+    return w;
+}
+
+size_t ffn_ws_bytes(int64_t rows, int groups, int H, int I, int dtype) {
+    (void)H;
+    if (elem_bytes(dtype) == 0) return 0;
+    return ffn_ws_layout(rows, groups, I, dtype).total;
+}
+
+size_t permute_ws_bytes(int64_t T, int k, int E) {
+    (void)T;
+    (void)k;
+    return align256((size_t)E * kPermuteWaves * 4 * 2);
+}
+
+size_t n_slices(size_t bytes, size_t chunk) { return bytes == 0 ? 0 : (bytes - 1) / chunk + 1; }
+
 std::vector<dwdp_chunk> make_plan(const dwdp_copy_src* srcs, int n_src, size_t chunk) {
     std::vector<dwdp_chunk> plan;
     size_t most = 0;
-    for (int s = 0; s < n_src; ++s) most = std::max(most, (srcs[s].bytes + chunk - 1) / chunk);
+    for (int s = 0; s < n_src; ++s) most = std::max(most, n_slices(srcs[s].bytes, chunk));
     for (size_t c = 0; c < most; ++c) {
         for (int s = 0; s < n_src; ++s) {
-            size_t n = (srcs[s].bytes + chunk - 1) / chunk;
+            size_t n = n_slices(srcs[s].bytes, chunk);
             if (c >= n) continue;
             dwdp_chunk ch{};
             ch.source = s;

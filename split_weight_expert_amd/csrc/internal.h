@@ -10,9 +10,22 @@
 namespace dwdp {
 
 constexpr int kMaxCopySources = 64;
+constexpr int kBmMin = 32;             // smallest expert-GEMM tile height (sizes the m-tile tables)
+constexpr size_t kMTileBytes = 16;     // one entry of an m-tile table
+constexpr int kPermuteWaves = 16;      // waves per count / scatter workgroup of the permutation
+
+// Grouped-FFN workspace: A [rows, I] in the activation type (+ its fp8 scales [rows, I/128]), the
+// m-tile prefix [G+1] and two m-tile tables, each part 256-byte aligned; the tables are sized for
+// the smallest tile height, so any tile choice fits.
+struct FfnWs {
+    size_t a, a_scale, pre, mt, mt_by_size, total;
+};
+FfnWs ffn_ws_layout(int64_t rows, int groups, int I, int dtype);
 
 size_t elem_bytes(int dtype);
 void record_layout(int H, int I, int w_dtype, size_t* w2, size_t* s13, size_t* s2, size_t* total);
+// Slices of a source of `bytes` bytes cut into `chunk`-byte pieces (no sum that could wrap).
+size_t n_slices(size_t bytes, size_t chunk);
 std::vector<dwdp_chunk> make_plan(const dwdp_copy_src* srcs, int n_src, size_t chunk);
 int check_sources(const dwdp_copy_src* srcs, int n_src, size_t chunk);
 

@@ -18,7 +18,7 @@
 namespace dwdp {
 namespace {
 
-constexpr int kWaves = 16;          // waves per count / scatter workgroup
+constexpr int kWaves = kPermuteWaves;   // waves per count / scatter workgroup
 constexpr int kPerLane = 16;        // consecutive entries per lane per step
 constexpr int kStep = 64 * kPerLane;
 
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(1024) void count_kernel(const int32_t* __restrict__
 
 __global__ __launch_bounds__(1024) void offsets_kernel(const int32_t* __restrict__ wave_counts, int E, int shared,
                                                        int64_t T, int64_t R, int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ wave_base) {
+                                                       int32_t* __restrict__ wave_base, int32_t* __restrict__ perm_src) {
     __shared__ int wsum[16];
     __shared__ int carry_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -113,6 +113,10 @@ __global__ __launch_bounds__(1024) void offsets_kernel(const int32_t* __restrict
         offsets[E] = (int32_t)R;                 // equals the count total when every index is valid
         if (shared) offsets[E + 1] = (int32_t)(R + T);
     }
+    // Rows of dropped entries (indices outside [0, E)): the count total falls short of R by their
+    // number, and rows [total, R) close the last routed group.  They read token 0, so every row the
+    // grouped FFN computes has a defined source; the combine never reads them (their inv_perm is -1).
+    for (int64_t r = (int64_t)carry_s + tid; r < R; r += 1024) perm_src[r] = 0;
 }
 
 __global__ __launch_bounds__(1024) void scatter_kernel(const int32_t* __restrict__ idx, int64_t N, int k, int E,
@@ -218,12 +222,6 @@ __global__ __launch_bounds__(256) void gather_fp8_kernel(const uint16_t* __restr
 
 }  // namespace
 
-size_t permute_ws_bytes(int64_t T, int k, int E) {
-    (void)T;
-    (void)k;
-    return ((size_t)E * kWaves * 4 * 2 + 255) & ~size_t(255);
-}
-
 }  // namespace dwdp
 
 using namespace dwdp;
@@ -258,7 +256,8 @@ extern "C" int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, in
     int32_t* wave_counts = static_cast<int32_t*>(ws);
     int32_t* wave_base = wave_counts + (size_t)E * kWaves;
     hipLaunchKernelGGL(count_kernel, dim3(E), dim3(1024), 0, st, topk_idx, N, seg, wave_counts);
-    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, wave_counts, E, shared, T, R, offsets, wave_base);
+    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, wave_counts, E, shared, T, R, offsets, wave_base,
+                       perm_src);
     hipLaunchKernelGGL(scatter_kernel, dim3(E), dim3(1024), 0, st, topk_idx, N, k, E, seg, wave_base, perm_src, inv_perm);
     if (!gather) {
         if (shared) hipLaunchKernelGGL(shared_rows_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, perm_src, R, T);

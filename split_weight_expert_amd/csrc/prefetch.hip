@@ -167,10 +167,10 @@ extern "C" int dwdp_prefetch_chunks(void* dst, const dwdp_copy_src* srcs, int n_
             a.src[s] = static_cast<const uint8_t*>(srcs[s].src);
             a.dst_off[s] = srcs[s].dst_offset;
             a.bytes[s] = srcs[s].bytes;
-            const int64_t nc = (int64_t)((srcs[s].bytes + chunk_bytes - 1) / chunk_bytes);
-            DWDP_REQUIRE(nc < ((int64_t)1 << 31), "too many slices for one source");
+            const size_t nc = n_slices(srcs[s].bytes, chunk_bytes);
+            DWDP_REQUIRE(nc < ((size_t)1 << 31), "too many slices for one source");
             a.nchunks[s] = (int32_t)nc;
-            rounds = std::max(rounds, nc);
+            rounds = std::max(rounds, (int64_t)nc);
         }
         a.max_rounds = (int32_t)rounds;
     }

@@ -85,8 +85,18 @@ class ExpertStore:
             api.pack_weights(q13, w13, FP8_E4M3, stream)
             api.pack_weights(q2, w2, FP8_E4M3, stream)
 
+    def check_placement(self, placement) -> None:
+        """Every (buffer, slot) must name a record inside this store: the C ABI cannot check it, since it
+        does not know the buffers' sizes, and the GEMM would read past the allocation."""
+        for g, (buf, slot) in enumerate(placement):
+            if not 0 <= buf < len(self.buffers):
+                raise ValueError(f"group {g}: buffer {buf} is not one of the store's {len(self.buffers)} buffers")
+            if not 0 <= slot < self.slots[buf]:
+                raise ValueError(f"group {g}: slot {slot} is outside buffer {buf}'s {self.slots[buf]} records")
+
     def table(self, placement, device="cuda") -> torch.Tensor:
         """Device pointer table for placement = [(buffer, slot) for each group]."""
+        self.check_placement(placement)
         t = api.fill_expert_table([b.data_ptr() for b in self.buffers], [p[0] for p in placement],
                                   [p[1] for p in placement], self.H, self.I, self.w_dtype)
         return api.table_to_device(t, device)

@@ -169,3 +169,32 @@ def test_workspace_sizes_grow_with_rows():
     b = api.workspace_bytes(api.OP_GROUPED_FFN, 64, 8, 256, 7168, 2048, 1, 1)
     assert a >= 73728 * 2048 * 2 and b >= 576 * 2048 * 2 and a > b
     assert api.workspace_bytes(api.OP_PERMUTE, 8192, 8, 256, 7168, 2048, 1, 1) > 0
+
+
+def test_grouped_ffn_rejects_shapes_outside_the_documented_limits(lib):
+    """The header's limits are what the library enforces: f32 needs H % 64 and I % 32, bf16/fp8 H % 256 and
+    I % 128, fp8 also H, I <= 8192."""
+    f = lib.dwdp_moe_grouped_ffn
+    E_ = lib_mod.DWDP_ERR_INVALID_ARG
+    ws = 1 << 40
+    for H, I, dt in ((96, 128, 0), (256, 48, 0), (7040, 2048, 1), (7168, 2000, 1), (8448, 2048, 2)):
+        expect(E_, f(FAKE, 9, FAKE, FAKE, FAKE, 128, H, I, dt, FAKE, FAKE, ws, None), lib, "H")
+    for H, I, dt in ((64, 32, 0), (256, 128, 1), (8192, 8192, 2)):   # accepted shapes fail later (on `rows`)
+        rc = f(FAKE, 9, FAKE, FAKE, FAKE, -1, H, I, dt, FAKE, FAKE, ws, None)
+        assert rc == E_ and "rows" in lib.dwdp_last_error().decode(), (H, I, dt)
+
+
+def test_store_rejects_placements_outside_its_buffers():
+    """ExpertStore.table checks every (buffer, slot) against the store before filling the pointer table (the
+    C ABI cannot: it does not know the buffers' sizes)."""
+    import torch
+
+    from split_weight_expert_amd import ExpertStore
+    st = ExpertStore(256, 128, lib_mod.F32, [2, 3], device="cpu")
+    good = [(0, 0), (0, 1), (1, 2)]
+    t = st.table(good, "cpu")
+    assert t.numel() == 32 * len(good)
+    for bad in ([(0, 2)], [(1, 3)], [(2, 0)], [(0, -1)], [(-1, 0)]):
+        with pytest.raises(ValueError):
+            st.table(good + bad, "cpu")
+    del torch
