@@ -171,22 +171,24 @@ def expert_ffn_parts(X, wg, wu, wd, precision: str) -> dict:
 
     X and the weights are the prepared values (see prepare_tokens / prepare_weights).  Returns
     A (the intermediate as the down projection consumes it, after the policy's rounding point),
-    A_codes and A_scales (fp8 only: the E4M3 codes and group scales of A) and Y.
+    A_pre, A_codes and A_scales (fp8 only: the fp32 value of A that is quantised, its E4M3 codes
+    and its group scales) and Y.
     """
     X = np.asarray(X, np.float64)
     G = X @ wg.T
     U = X @ wu.T
     A = silu(G) * U
-    codes = scales = None
+    pre = codes = scales = None
     if precision == "bf16":
         A = bf16_round(A)
     elif precision == "fp8":
-        codes, scales = quantize_groups(A.astype(np.float32))
+        pre = A.astype(np.float32)
+        codes, scales = quantize_groups(pre)
         A = dequant_groups(codes, scales)
     Y = A @ wd.T
     if precision in ("bf16", "fp8"):
         Y = bf16_round(Y)
-    return dict(A=A, A_codes=codes, A_scales=scales, Y=Y)
+    return dict(A=A, A_pre=pre, A_codes=codes, A_scales=scales, Y=Y)
 
 
 def expert_ffn(X, wg, wu, wd, precision: str) -> np.ndarray:

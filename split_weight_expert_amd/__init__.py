@@ -9,6 +9,6 @@ from . import _lib
 _lib.load()
 
 from . import api  # noqa: E402,F401
-from .moe import ExpertStore, MoEBlock, dwdp_placement  # noqa: E402,F401
+from .moe import DWDPPipeline, ExpertStore, LayerWeights, MoEBlock, dwdp_placement  # noqa: E402,F401
 
-__all__ = ["api", "ExpertStore", "MoEBlock", "dwdp_placement"]
+__all__ = ["api", "DWDPPipeline", "ExpertStore", "LayerWeights", "MoEBlock", "dwdp_placement"]

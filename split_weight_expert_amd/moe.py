@@ -195,14 +195,143 @@ class MoEBlock:
             api.moe_grouped_ffn_tokens(stage, table, self.E + self.shared, b.offsets, b.perm_src, b.x_tokens,
                                        b.x_q_scale, self.H, self.I, self.w_dtype, b.y_perm, b.ws_ffn, stream)
 
-    def combine(self, b: BlockBuffers, stream=None):
-        api.combine(b.y_perm, b.inv_perm, b.w, self.shared, b.y, stream)
+    def combine(self, b: BlockBuffers, stream=None, out=None):
+        api.combine(b.y_perm, b.inv_perm, b.w, self.shared, b.y if out is None else out, stream)
 
-    def forward(self, x, w_router, bias, table, stream=None) -> BlockBuffers:
-        """The whole block on `stream`; results stay in the returned buffers."""
+    def forward(self, x, w_router, bias, table, stream=None, out=None) -> BlockBuffers:
+        """The whole block on `stream`; results stay in the returned buffers (y in `out` if given)."""
         b = self.buffers(x.shape[0])
         self.route(x, w_router, bias, b, stream)
         self.permute(x, b, stream)
         self.ffn(table, b, stream)
-        self.combine(b, stream)
+        self.combine(b, stream, out)
         return b
+
+
+@dataclass
+class LayerWeights:
+    """One MoE layer in the DWDP layout of a rank.
+
+    resident: the rank's own records of the layer, experts [0, n_local) then the shared expert, in
+    one device buffer (the resident partition, DWDP paper summary §2).  sources: where the layer's
+    other E - n_local expert records are pulled from, as (device pointer, offset in the slot set,
+    bytes) -- on one GPU, separate device allocations stand in for the peers' HBM; record e sits at
+    offset (e - n_local) * record_bytes of the slot set.
+    """
+    w_router: torch.Tensor
+    bias: torch.Tensor | None
+    resident: torch.Tensor
+    sources: list
+
+
+class DWDPPipeline:
+    """Layer-ahead prefetch over a double-buffered slot area (DWDP paper summary §2, §4.3.2).
+
+    While layer l computes on the compute stream from slot set l % 2, a copy stream pulls layer l+1's
+    non-local experts into slot set (l + 1) % 2 in fixed-size slices, round-robin over the sources.
+    Two hazards are ordered with events: layer l waits for the copy that filled its slot set, and a
+    copy into a slot set waits for the layer that last read it.  The layer time is then
+    max(compute, copy) (the layer-wise model of the pages, §3), not their sum.
+
+    The block reads each layer's weights through a pointer table over two buffers -- the layer's
+    resident records and the current slot set -- so nothing is merged.  Only the MoE blocks run here
+    (a model without attention): layer l+1's input is layer l's output.
+    """
+
+    def __init__(self, H: int, I: int, E: int, k: int, shared: int, dtype: str, n_local: int, device="cuda",
+                 slot_sets=None, chunk_bytes: int = 4 << 20, engine: int = api.COPY_KERNEL,
+                 max_workgroups: int = 48):
+        self.H, self.I, self.E, self.k, self.shared, self.n_local = H, I, E, k, shared, n_local
+        self.w_dtype = DTYPES[dtype]
+        self.device = torch.device(device)
+        self.rec = api.expert_record_bytes(H, I, self.w_dtype)
+        self.n_pre = E - n_local
+        if slot_sets is None:
+            slot_sets = [torch.empty(max(self.n_pre, 1) * self.rec, dtype=torch.uint8, device=self.device)
+                         for _ in range(2)]
+        assert len(slot_sets) == 2 and all(t.numel() >= self.n_pre * self.rec for t in slot_sets)
+        self.slot_sets = slot_sets
+        self.chunk_bytes, self.engine, self.max_workgroups = chunk_bytes, engine, max_workgroups
+        self.block = MoEBlock(H, I, E, k, shared, dtype, self.device)
+        self.copy_stream = torch.cuda.Stream(self.device)
+        self._last_read = [None, None]      # event of the last layer that read each slot set
+        self._tables = {}
+
+    def placement(self):
+        """(buffer, slot) of every group: 0 = the layer's resident records, 1 = the current slot set."""
+        pl = [(0, e) if e < self.n_local else (1, e - self.n_local) for e in range(self.E)]
+        if self.shared:
+            pl.append((0, self.n_local))
+        return pl
+
+    def table(self, layer: LayerWeights, s: int) -> torch.Tensor:
+        key = (layer.resident.data_ptr(), s)
+        if key not in self._tables:
+            assert layer.resident.numel() >= (self.n_local + self.shared) * self.rec, "resident buffer too small"
+            pl = self.placement()
+            t = api.fill_expert_table([layer.resident.data_ptr(), self.slot_sets[s].data_ptr()],
+                                      [p[0] for p in pl], [p[1] for p in pl], self.H, self.I, self.w_dtype)
+            self._tables[key] = api.table_to_device(t, self.device)
+        return self._tables[key]
+
+    def check_sources(self, layer: LayerWeights):
+        for _, off, n in layer.sources:
+            assert 0 <= off and off + n <= self.n_pre * self.rec, "a source lands outside the slot set"
+
+    def prefetch(self, layer: LayerWeights, s: int, wait=None, done=None):
+        """Enqueue the pull of `layer`'s non-local records into slot set s on the copy stream."""
+        api.prefetch_chunks(self.slot_sets[s].data_ptr(), layer.sources, self.chunk_bytes, engine=self.engine,
+                            max_workgroups=self.max_workgroups, copy_stream=self.copy_stream, wait_event=wait,
+                            done_event=done)
+
+    def forward(self, x: torch.Tensor, layers, outputs=None, before_copy=None, before_compute=None,
+                after_layer=None, chain: bool = True) -> torch.Tensor:
+        """Run the layers in order on the current stream, each on the previous one's output (or, with
+        chain=False, every layer on x: a benchmark of layers with a fixed input distribution).
+
+        outputs: optional list of L [T, H] tensors that receive every layer's output (else two
+        alternating buffers are used and only the last output is returned).  The hooks are called at
+        enqueue time: before_copy(l) with the copy stream current, before layer l's pull is enqueued;
+        before_compute(l) and after_layer(l, block_buffers) with the compute stream current, around
+        layer l's block.  Returns the last layer's output.
+        """
+        comp = torch.cuda.current_stream(self.device)
+        L = len(layers)
+        for lw in layers:
+            self.check_sources(lw)
+        T = x.shape[0]
+        if outputs is None:
+            bufs = [torch.empty(T, self.H, dtype=x.dtype, device=self.device) for _ in range(min(L, 2))]
+            outputs = [bufs[l % 2] for l in range(L)]
+        copy_done = [torch.cuda.Event(), torch.cuda.Event()]
+        # the copy stream must not start before everything already enqueued on the compute stream
+        # that produced the sources or this call's input
+        start = torch.cuda.Event()
+        start.record(comp)
+        self.copy_stream.wait_event(start)
+
+        def pull(l, s):
+            with torch.cuda.stream(self.copy_stream):
+                if before_copy is not None:
+                    before_copy(l)
+            self.prefetch(layers[l], s, wait=self._last_read[s], done=copy_done[s])
+
+        if L:
+            pull(0, 0)
+        for l in range(L):
+            s = l % 2
+            if l + 1 < L:
+                pull(l + 1, 1 - s)
+            comp.wait_event(copy_done[s])
+            if before_compute is not None:
+                before_compute(l)
+            lw = layers[l]
+            b = self.block.forward(x, lw.w_router, lw.bias, self.table(lw, s), out=outputs[l])
+            if after_layer is not None:
+                after_layer(l, b)
+            ev = torch.cuda.Event()
+            ev.record(comp)
+            self._last_read[s] = ev
+            if chain:
+                x = outputs[l]
+        return outputs[L - 1] if L else x

@@ -8,7 +8,11 @@ import torch
 import synth
 from oracle import moe as omoe
 
-TOL = {"f32": dict(max=1e-5, mean=1e-5), "bf16": dict(max=2e-2, mean=2e-3), "fp8": dict(max=6e-2, mean=6e-2)}
+# Relative-error bars (max over elements, mean over elements) of |y - r| / max(|r|, rms(r)).  The fp32,
+# bf16 and fp8 maxima are the stated ones.  fp8 states no mean; its mean bar is a tenth of its maximum,
+# the same ratio as bf16's, so that a widespread error fails the mean before any single element fails
+# the maximum.
+TOL = {"f32": dict(max=1e-5, mean=1e-5), "bf16": dict(max=2e-2, mean=2e-3), "fp8": dict(max=6e-2, mean=6e-3)}
 
 
 def need_gpu():
@@ -89,22 +93,52 @@ def ffn_ws_a(ws: torch.Tensor, rows: int, I: int, sel=None):
     return codes.cpu().numpy(), scales.cpu().numpy()
 
 
-def check_fp8_rows(y, a_codes, a_scales, parts, wd, rms, what=""):
+def e4m3_rounding_distance(v_scaled, codes):
+    """Distance from each value v (scaled units) to the interval of values that round to the given E4M3
+    code (0 where v rounds to it): the interval runs between the midpoints to the neighbouring code
+    values, and past 448 for the largest code (saturation)."""
+    from oracle import codecs
+    vals = np.unique(codecs.E4M3_VALUES[np.isfinite(codecs.E4M3_VALUES)])      # sorted, one zero
+    c = codecs.e4m3_decode(codes)
+    i = np.searchsorted(vals, c)
+    lo = np.where(i > 0, 0.5 * (vals[np.maximum(i - 1, 0)] + c), -np.inf)
+    hi = np.where(i < len(vals) - 1, 0.5 * (vals[np.minimum(i + 1, len(vals) - 1)] + c), np.inf)
+    v = np.asarray(v_scaled, np.float64)
+    return np.maximum(0.0, np.maximum(lo - v, v - hi))
+
+
+# A re-quantisation flip of an fp8 A code is allowed only where the GPU's code is the rounding of a value
+# within FLIP_REL * |v| + FLIP_ABS of the oracle's fp32 value v of A (scaled units, in which the group's
+# largest magnitude is 448).  GEMM1 sums each 64-wide fp8 product block in
+# the matrix core, whose accumulation of fp8 products is measured here to carry up to about 5e-5 of
+# relative error on the largest element of a group (the group scales, amax / 448, of the 16K-token
+# fp8 layer differ from the oracle's by up to 4.9e-5), then folds K / 128 block sums with fp32 scale
+# products, and SwiGLU uses the hardware exponential.  The windows are about four times that: the
+# scale tolerance and the relative window 2e-4, and an absolute window of 1e-4 of the group maximum
+# for elements where G and U cancel (the error of a dot product follows the sum of its terms'
+# magnitudes, not its result).  With that error about 1.6e-3 of the 16K-token layer's A codes land on
+# another code (all within the window); the rate bar is three times that.
+FLIP_REL = 2e-4
+FLIP_ABS = 448.0 * 1e-4
+SCALE_RTOL = 2e-4
+FLIP_RATE = 5e-3
+
+
+def check_fp8_rows(y, a_codes, a_scales, parts, wd, rms, what="", stats=None):
     """fp8 expert rows against the oracle, allowing for re-quantisation flips of A.
 
     A is re-quantised to E4M3 from an fp32 value that the GPU and the oracle accumulate in
-    different orders, so a value within rounding distance of a midpoint between two codes may
-    land on the neighbouring code (and a group's amax, with it the scale, differs by the fp32
-    accumulation error of GEMM1, up to about 1e-4 relative).  Rows whose A codes equal the
-    oracle's must meet the fp8 tolerance.  At most 1 in 100 codes may differ, each by one code
-    step plus 1e-4 of its group's amax, and the rows holding them must stay within the
-    tolerance plus the flipped codes' effect through the down projection (plus one bf16
-    rounding).
+    different orders, so a value within rounding distance of the rounding boundary between two
+    codes may land on the neighbouring code.  Rows whose A codes equal the oracle's must meet the
+    fp8 tolerance.  A differing code must be the rounding of a value inside the window above around
+    the oracle's fp32 A (before its rounding); at most FLIP_RATE of the codes may differ; the scales agree to SCALE_RTOL; and the rows holding flips stay within the
+    tolerance plus the flipped codes' effect through the down projection (plus one bf16 rounding).
 
     y: GPU rows [n, H]; a_codes / a_scales: the GPU's A of the same rows; parts:
     oracle.moe.expert_ffn_parts of the same rows; wd: the prepared down weights [H, I];
-    rms: rms of the whole reference the rows belong to.  Returns (rows with flips, max rel of
-    the clean rows).
+    rms: rms of the whole reference the rows belong to; stats: optional dict that accumulates
+    codes, flips and the largest flip distance (in units of the allowed window).
+    Returns (rows with flips, max rel of the clean rows).
     """
     from oracle import codecs
     r = parts["Y"]
@@ -116,19 +150,29 @@ def check_fp8_rows(y, a_codes, a_scales, parts, wd, rms, what=""):
     clean = ~flip
     mx = float((np.abs(y - r) / den)[clean].max()) if clean.any() else 0.0
     assert mx <= tol, f"{what}: clean rows max rel {mx:.3e} (tol {tol})"
-    assert diff.mean() <= 1e-2, f"{what}: {diff.sum()} of {diff.size} A codes differ"
-    # the scales follow each group's amax, which carries the fp32 accumulation error of GEMM1
-    np.testing.assert_allclose(a_scales, parts["A_scales"], rtol=2e-4, atol=0, err_msg=f"{what}: A scales")
-    if flip.any():
+    np.testing.assert_allclose(a_scales, parts["A_scales"], rtol=SCALE_RTOL, atol=0, err_msg=f"{what}: A scales")
+    worst = 0.0
+    if diff.any():
+        ri, ci = np.nonzero(diff)
+        co, cg = parts["A_codes"][ri, ci], a_codes[ri, ci]
+        # the GPU's code must be the rounding of a value within the window around the oracle's fp32 A
+        # before rounding (A_pre), in scaled units
+        v_scaled = parts["A_pre"][ri, ci] / parts["A_scales"][ri, ci // 128]
+        d = e4m3_rounding_distance(v_scaled, cg)
+        win = FLIP_REL * np.abs(v_scaled) + FLIP_ABS
+        worst = float((d / win).max())
+        assert worst <= 1.0, f"{what}: a flipped A code is {worst:.2f} windows from the oracle's A"
+        rate = diff.mean()
+        assert rate <= FLIP_RATE, f"{what}: {diff.sum()} of {diff.size} A codes differ ({rate:.2e})"
         g = codecs.e4m3_decode(a_codes[flip]).reshape(flip.sum(), -1, 128) * a_scales[flip][:, :, None]
-        o = parts["A"][flip].reshape(flip.sum(), -1, 128)
         g = g.reshape(flip.sum(), -1)
-        o = o.reshape(flip.sum(), -1)
-        # neighbouring codes: one E4M3 step (1/8 of the larger magnitude, or one subnormal step) plus
-        # the fp32 accumulation error of A, taken as 1e-4 of its group's amax (= 448 * scale)
-        sc = np.repeat(np.maximum(a_scales[flip], parts["A_scales"][flip]), 128, axis=1)
-        step = np.maximum(np.abs(g), np.abs(o)) / 8.0 + sc * 2.0 ** -9 + 1e-4 * 448.0 * sc
-        assert (np.abs(g - o) <= step * (1 + 1e-6)).all(), f"{what}: a flipped A code is not a neighbour"
+        o = parts["A"][flip].reshape(flip.sum(), -1)
         bound = tol * den[flip] + np.abs(g - o) @ np.abs(wd).T * (1 + 1e-6) + np.abs(r[flip]) * 2.0 ** -8
         assert (np.abs(y[flip] - r[flip]) <= bound).all(), f"{what}: a row with flipped A codes is off"
+    if stats is not None:
+        srel = np.abs(a_scales / parts["A_scales"] - 1.0)
+        stats["scale_rel_max"] = max(stats.get("scale_rel_max", 0.0), float(srel.max()))
+        stats["codes"] = stats.get("codes", 0) + int(diff.size)
+        stats["flips"] = stats.get("flips", 0) + int(diff.sum())
+        stats["worst_window"] = max(stats.get("worst_window", 0.0), worst)
     return int(flip.sum()), mx

@@ -597,3 +597,145 @@ def test_empty_batch_is_a_no_op_for_every_step():
     api.combine(torch.empty(0, H, dtype=torch.bfloat16, device=DEV), idx, w, 1, y)
     torch.cuda.synchronize()
     assert (off.cpu() == -5).all()         # T = 0 returns before anything is written
+
+
+# --------------------------------------------------------------------------------------- dropped entries
+
+def test_permute_and_combine_drop_out_of_range_indices():
+    """topk_idx entries outside [0, E) are dropped (include/dwdp.h, dwdp_permute): counted in no expert,
+    inv_perm -1, skipped by the combine; offsets[E] stays T*k and the rows closing the last routed group
+    read token 0 (defined, never read back)."""
+    from split_weight_expert_amd import api
+    T, k, E, H, S = 300, 4, 16, 256, 1
+    rng = np.random.default_rng(17)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    bad = [(0, 1, -1), (5, 0, E), (17, 3, E + 5), (120, 2, -7), (299, 0, 1 << 20)]
+    for t, j, v in bad:
+        idx[t, j] = v
+    valid = (idx >= 0) & (idx < E)
+    x = torch.randn(T, H, device=DEV).to(torch.bfloat16)
+    _, _, off, ps, ip = run_permute(idx, E, S, x, api.BF16)
+    # the expected permutation of the valid entries: experts ascending, then flattened t*k+j
+    flat = np.flatnonzero(valid.ravel())
+    order = flat[np.argsort(idx.ravel()[flat], kind="stable")]
+    counts = np.bincount(idx.ravel()[flat], minlength=E)
+    n_valid, D = len(order), T * k - len(order)
+    exp_off = np.concatenate([[0], np.cumsum(counts)[:-1], [T * k, T * k + T]])
+    np.testing.assert_array_equal(off, exp_off)
+    exp_ip = np.full(T * k, -1, np.int64)
+    exp_ip[order] = np.arange(n_valid)
+    np.testing.assert_array_equal(ip.ravel(), exp_ip)
+    np.testing.assert_array_equal(ps[:n_valid], order // k)
+    np.testing.assert_array_equal(ps[n_valid:T * k], np.zeros(D, np.int32))       # the dropped rows: token 0
+    np.testing.assert_array_equal(ps[T * k:], np.arange(T))
+    # the combine skips the dropped slots
+    rows = T * k + S * T
+    yp = torch.randn(rows, H, device=DEV).to(torch.bfloat16)
+    w = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    api.combine(yp, torch.from_numpy(ip).to(DEV), torch.from_numpy(w).to(DEV), S, y)
+    torch.cuda.synchronize()
+    ypn = to_np(yp)
+    ref = np.stack([omoe.combine(ypn[ip[t][valid[t]]], w[t][valid[t]], ypn[T * k + t], "bf16") for t in range(T)])
+    assert_close(to_np(y), ref, "bf16", "combine with dropped slots")   # fp32 sums vs fp64: one rounding apart
+
+
+# --------------------------------------------------------------------------------------- deep K, every tail
+
+# Group sizes chosen so that the last m-tile of the groups holds every row count the kernels have a
+# variant for.  bf16 runs 256-row tiles (mean rows per group >= 192): tails of 20, 50, 80, 120, 180,
+# 250 and 256 rows (1..8 active 32-row blocks, spread over the two 128-row halves).  fp8 runs 128-row
+# tiles: tails of 20, 50, 80, 120 and 128 rows.  An empty group is included.  K = 2048 (GEMM1) and
+# 1024 (GEMM2) are deep enough for the steady-state loops of both DMA rings (bf16: 64 and 32 K steps
+# against NS + P = 8; fp8: 16 and 8 against NS + P - 1 = 4).
+TAIL_CASES = {
+    "bf16": dict(H=2048, I=1024, sizes=[276, 306, 336, 376, 436, 506, 512, 0, 20]),
+    "fp8": dict(H=2048, I=1024, sizes=[148, 178, 208, 248, 256, 0, 600, 20]),
+}
+
+
+def normal_expert(rng, H, I):
+    """(Wg, Wu, Wd) float32 ~ N(0, 1/fan_in) from numpy's normal generator (true normal tails)."""
+    return (rng.normal(0, H ** -0.5, size=(I, H)).astype(np.float32),
+            rng.normal(0, H ** -0.5, size=(I, H)).astype(np.float32),
+            rng.normal(0, I ** -0.5, size=(H, I)).astype(np.float32))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_grouped_ffn_every_tail_variant_deep_k(dt):
+    """Every y_perm row of a grouped FFN whose groups end on every tile-tail variant, at K large enough
+    for the steady-state DMA ring loops, against the oracle's expert FFN; inputs from numpy's normal
+    generator (unbounded tails, which set the fp8 group maxima)."""
+    from split_weight_expert_amd import ExpertStore, api
+    from split_weight_expert_amd.moe import DTYPES
+    c = TAIL_CASES[dt]
+    H, I, sizes = c["H"], c["I"], c["sizes"]
+    E, k, S = len(sizes), 1, 1
+    T = int(sum(sizes))
+    rng = np.random.default_rng(123 if dt == "bf16" else 321)
+    idx = np.repeat(np.arange(E), sizes).astype(np.int32)[rng.permutation(T)].reshape(T, 1)
+    x = rng.normal(0, 1, size=(T, H)).astype(np.float32)
+    x[7, 5] = 9.0                                              # an outlier sets one group's scale
+    experts = [normal_expert(rng, H, I) for _ in range(E + S)]
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()     # tokens enter as bf16 (fp8 too)
+    if dt == "bf16":                                           # bf16 layers hold bf16 weights; fp8 quantises fp32
+        experts = [tuple(torch.from_numpy(w).to(torch.bfloat16).float().numpy() for w in ex) for ex in experts]
+    wd = DTYPES[dt]
+    G = E + S
+    store = ExpertStore(H, I, wd, [(G + 1) // 2, G // 2], device=DEV)
+    pl = [(g % 2, g // 2) for g in range(G)]                   # groups alternate between two buffers
+    for g, (b_, s_) in enumerate(pl):
+        ws_ = [torch.from_numpy(w).to(DEV) for w in experts[g]]
+        if dt == "bf16":
+            ws_ = [w.to(torch.bfloat16) for w in ws_]
+        store.load(b_, s_, *ws_)
+    table = store.table(pl, DEV)
+    xt = torch.from_numpy(x).to(DEV, torch.bfloat16)
+    rows = T * (k + S)
+    off = torch.empty(G + 1, dtype=torch.int32, device=DEV)
+    ps = torch.empty(rows, dtype=torch.int32, device=DEV)
+    ip = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    wsp = torch.empty(api.workspace_bytes(api.OP_PERMUTE, T, k, E, H, I, wd, S), dtype=torch.uint8, device=DEV)
+    api.permute(torch.from_numpy(idx).to(DEV), E, S, xt, api.BF16, None, None, off, ps, ip, wsp)
+    xq = xs = None
+    if dt == "fp8":
+        xq = torch.empty(T, H, dtype=torch.uint8, device=DEV)
+        xs = torch.empty(T, H // 128, dtype=torch.float32, device=DEV)
+        api.quantize_tokens_fp8(xt, xq, xs)
+    y_perm = torch.empty(rows, H, dtype=torch.bfloat16, device=DEV)
+    wsf = torch.empty(api.workspace_bytes(api.OP_GROUPED_FFN, T, k, E, H, I, wd, S), dtype=torch.uint8, device=DEV)
+    api.moe_grouped_ffn_tokens(0, table, G, off, ps, xq if dt == "fp8" else xt, xs, H, I, wd, y_perm, wsf)
+    torch.cuda.synchronize()
+    o, p, _, counts = omoe.permute(idx, E, S)
+    np.testing.assert_array_equal(off.cpu().numpy(), o)
+    np.testing.assert_array_equal(ps.cpu().numpy(), p)
+    np.testing.assert_array_equal(counts, sizes)
+    y = to_np(y_perm).astype(np.float64)
+    X = omoe.prepare_tokens(x[p], dt)
+    if dt == "bf16":
+        ref = np.zeros_like(y)
+        for g in range(G):
+            r0, r1 = o[g], o[g + 1]
+            if r1 > r0:
+                ref[r0:r1] = omoe.expert_ffn(X[r0:r1], *omoe.prepare_weights(*experts[g], dt), dt)
+        mx, mn = assert_close(y, ref, dt, "grouped ffn, every tail, deep K")
+        print(f"[tails bf16] rows {rows} max rel {mx:.2e} mean rel {mn:.2e}", flush=True)
+        return
+    codes, scales = ffn_ws_a(wsf, rows, I)
+    parts = {}
+    for g in range(G):
+        r0, r1 = o[g], o[g + 1]
+        if r1 > r0:
+            wts = omoe.prepare_weights(*experts[g], dt)
+            parts[g] = (omoe.expert_ffn_parts(X[r0:r1], *wts, dt), wts[2])
+    ref = np.concatenate([parts[g][0]["Y"] for g in sorted(parts)])
+    rms = np.sqrt((ref ** 2).mean())
+    stats = {}
+    for g, (pt, w2) in parts.items():
+        r0, r1 = o[g], o[g + 1]
+        check_fp8_rows(y[r0:r1], codes[r0:r1], scales[r0:r1], pt, w2, rms, f"fp8 tails group {g}", stats)
+    mx, mn = rel_err(y, ref)
+    assert mx <= TOL["fp8"]["max"] and mn <= TOL["fp8"]["mean"]
+    print(f"[tails fp8] rows {rows} max rel {mx:.2e} mean rel {mn:.2e}; A codes {stats['codes']}, "
+          f"flips {stats['flips']} ({stats['flips'] / stats['codes']:.2e}), worst flip "
+          f"{stats['worst_window']:.3f} windows, scales within {stats['scale_rel_max']:.1e}", flush=True)
