@@ -207,6 +207,25 @@ int dwdp_moe_grouped_ffn_tokens(int stage, const dwdp_expert_ptrs* table, int n_
                                 int64_t rows, int H, int I, int w_dtype, void* y_perm, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/* dwdp_moe_grouped_ffn_tokens without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * workspace is a fixed array inside the library, dwdp_static_scratch_bytes() = 64 MiB on each GPU the
+ * library runs on, held until the process ends.  The call allocates nothing.  It computes exactly what
+ * dwdp_moe_grouped_ffn_tokens computes with the same arguments (bitwise), and rejects with
+ * DWDP_ERR_WORKSPACE, before anything is enqueued, a shape whose workspace
+ * (dwdp_workspace_bytes(DWDP_OP_GROUPED_FFN, ...)) exceeds that size -- with bf16 weights and I = 2048
+ * about 16K permuted rows, e.g. a decode batch of up to ~1800 tokens at top-8 plus a shared expert.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents: a stage-2 call
+ * reads the A left by the last stage-1 call on that GPU, and calls whose executions overlap on one GPU
+ * (other streams, other threads) race on the array and give undefined results. */
+int dwdp_moe_grouped_ffn_tokens_static(int stage, const dwdp_expert_ptrs* table, int n_groups,
+                                       const int32_t* offsets, const int32_t* perm_src, const void* x,
+                                       const float* x_scale, int64_t T, int64_t rows, int H, int I, int w_dtype,
+                                       void* y_perm, void* stream);
+
+/* Bytes of the fixed workspace array dwdp_moe_grouped_ffn_tokens_static uses (64 MiB). */
+size_t dwdp_static_scratch_bytes(void);
+
 /* Combine: y[t] = sum_{j<k} topk_w[t,j] * y_perm[inv_perm[t,j]] (+ y_perm[T*k + t]
  * when shared), summed in fp32 in slot order then the shared row, rounded once
  * to out_dtype.  y_perm is fp32 for out_dtype F32, bf16 otherwise.  The pages

@@ -47,6 +47,9 @@ SIGNATURES = {
                                           _vp]),
     "dwdp_moe_grouped_ffn_tokens": (_i32, [_i32, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp,
                                            _vp, _sz, _vp]),
+    "dwdp_moe_grouped_ffn_tokens_static": (_i32, [_i32, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32,
+                                                  _vp, _vp]),
+    "dwdp_static_scratch_bytes": (_sz, []),
     "dwdp_quantize_tokens_fp8": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "dwdp_combine": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
     "dwdp_prefetch_chunks": (_i32, [_vp, _vp, _i32, _sz, _i32, _i32, _vp, _vp, _vp]),

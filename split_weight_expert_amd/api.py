@@ -91,6 +91,20 @@ def moe_grouped_ffn_tokens(stage, table, n_groups, offsets, perm_src, x, x_scale
                                                        _stream(stream)))
 
 
+def moe_grouped_ffn_tokens_static(stage, table, n_groups, offsets, perm_src, x, x_scale, H, I, w_dtype, y_perm,
+                                  stream=None):
+    """moe_grouped_ffn_tokens with the library's fixed workspace array (no workspace argument)."""
+    rows = perm_src.shape[0]
+    T = x.shape[0]
+    _lib.check(_lib.load().dwdp_moe_grouped_ffn_tokens_static(stage, _ptr(table), n_groups, _ptr(offsets),
+                                                              _ptr(perm_src), _ptr(x), _ptr(x_scale), T, rows, H, I,
+                                                              w_dtype, _ptr(y_perm), _stream(stream)))
+
+
+def static_scratch_bytes() -> int:
+    return int(_lib.load().dwdp_static_scratch_bytes())
+
+
 def quantize_tokens_fp8(x, q, q_scale, stream=None):
     T, H = x.shape
     _lib.check(_lib.load().dwdp_quantize_tokens_fp8(_ptr(x), T, H, _ptr(q), _ptr(q_scale), _stream(stream)))

@@ -24,6 +24,7 @@
 //   * f32 (small shapes only): LDS-tiled FMA kernel with the same schedule.
 //   * Router (bf16): router_mfma_kernel, a plain two-stage MFMA tile kernel.
 #include <algorithm>
+#include <mutex>
 
 #include <type_traits>
 
@@ -1213,6 +1214,59 @@ extern "C" int dwdp_moe_grouped_ffn_tokens(int stage, const dwdp_expert_ptrs* ta
     DWDP_REQUIRE(rows == 0 || T >= 1, "T must be positive");
     return grouped_ffn(stage, table, n_groups, offsets, perm_src, x, x_scale, T, rows, H, I, w_dtype, y_perm, ws,
                        ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------------------ no-allocation variant
+// The grouped FFN's workspace (A, its fp8 scales and the tile schedule) in a fixed device array of the
+// library, for callers that cannot allocate.  In host code `scratch` names a host-side stand-in, not
+// the device array: its device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is ever passed on.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+    int dev = -1;
+    DWDP_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(DWDP_ERR_UNSUPPORTED, "device index beyond 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        DWDP_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (p == nullptr) return fail(DWDP_ERR_HIP, "hipGetSymbolAddress returned a null address for the scratch array");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DWDP_OK;
+}
+
+}  // namespace
+
+extern "C" size_t dwdp_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" int dwdp_moe_grouped_ffn_tokens_static(int stage, const dwdp_expert_ptrs* table, int n_groups,
+                                                  const int32_t* offsets, const int32_t* perm_src, const void* x,
+                                                  const float* x_scale, int64_t T, int64_t rows, int H, int I,
+                                                  int w_dtype, void* y_perm, void* stream) {
+    clear_error();
+    DWDP_REQUIRE(rows >= 0 && n_groups >= 1 && I > 0, "bad rows, n_groups or I");
+    DWDP_REQUIRE(w_dtype == DWDP_F32 || w_dtype == DWDP_BF16 || w_dtype == DWDP_FP8_E4M3, "unknown w_dtype");
+    const size_t need = ffn_ws_layout(rows, n_groups, I, w_dtype).total;
+    if (need > kStaticScratchBytes)
+        return fail(DWDP_ERR_WORKSPACE, "dwdp_moe_grouped_ffn_tokens_static: the workspace of " + std::to_string(rows) +
+                                            " rows needs " + std::to_string(need) + " bytes, more than the " +
+                                            std::to_string(kStaticScratchBytes) + "-byte static scratch");
+    if (rows == 0) return DWDP_OK;
+    void* ws = nullptr;
+    const int rc = scratch_address(&ws);
+    if (rc != DWDP_OK) return rc;
+    return dwdp_moe_grouped_ffn_tokens(stage, table, n_groups, offsets, perm_src, x, x_scale, T, rows, H, I, w_dtype,
+                                       y_perm, ws, kStaticScratchBytes, stream);
 }
 
 extern "C" int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups, const int32_t* offsets,
