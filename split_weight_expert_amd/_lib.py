@@ -9,7 +9,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "lib", "libdwdp.so")
+# DWDP_LIBRARY may name another build of the same library (e.g. one compiled with different tile settings)
+LIB_PATH = os.environ.get("DWDP_LIBRARY") or os.path.join(HERE, "lib", "libdwdp.so")
 
 DWDP_OK, DWDP_ERR_INVALID_ARG, DWDP_ERR_UNSUPPORTED, DWDP_ERR_WORKSPACE, DWDP_ERR_HIP = range(5)
 F32, BF16, FP8_E4M3 = 0, 1, 2

@@ -22,7 +22,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-u
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", src, "-o", obj]
+    # DWDP_EXTRA_FLAGS: compile-time options of the kernels (e.g. -DDWDP_FP8_BM256), space separated
+    extra = os.environ.get("DWDP_EXTRA_FLAGS", "").split()
+    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -65,6 +65,7 @@ struct GemmParams {
     int N;                          // GEMM1: I (A columns); GEMM2: H; router: E
     int K;
     int NT;                         // n-tiles
+    int msuper;                     // largest m super-block (m-tiles that run n-tile by n-tile together)
     int I;                          // GEMM1: first up row inside W13
     uint8_t* out;
     float* out_scale;               // GEMM1 fp8: A scales [rows, I/128]
@@ -89,10 +90,18 @@ __device__ __forceinline__ int64_t act_row(const GemmParams& p, int64_t prow) {
 // cluster's reuse stays inside one XCD's L2, while the round-robin over clusters spreads heavy and
 // light groups evenly over the eight XCDs.
 constexpr int kCluster = 32;
-// Inside a group, m-tiles are taken in super-blocks of up to kMSuper: the tiles of a super-block run
-// n-tile by n-tile with the m-tiles innermost, so a window of 32 running tiles reads about 4
-// activation slabs and 8 weight slabs instead of 32 of one kind.
-constexpr int kMSuper = 4;
+// Inside a group, m-tiles are taken in super-blocks of up to p.msuper: the tiles of a super-block run
+// n-tile by n-tile with the m-tiles innermost, so a window of 32 running tiles reads about msuper
+// activation slabs and 32 / msuper weight slabs instead of 32 of one kind.
+#ifndef DWDP_MSUPER_BF16
+#define DWDP_MSUPER_BF16 4
+#endif
+#ifndef DWDP_MSUPER_FP8
+#define DWDP_MSUPER_FP8 4
+#endif
+#ifndef DWDP_MSUPER_BALANCED
+#define DWDP_MSUPER_BALANCED 0
+#endif
 
 template <int BM, int KIND>
 __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
@@ -118,12 +127,32 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
     }
     const MTile m = p.mtiles[lin / p.NT];
     int rem = lin - m.m0 * p.NT;               // tile index inside the group
-    const int sb = rem / (kMSuper * p.NT);     // m super-block
-    const int ms = min(kMSuper, m.mc - sb * kMSuper);
-    rem -= sb * kMSuper * p.NT;
+    int ms, mfirst;
+    if (DWDP_MSUPER_BALANCED) {
+        // the group's m-tiles in ceil(mc / msuper) super-blocks of nearly equal size (the first `extra`
+        // ones a tile larger)
+        const int nsb = (m.mc + p.msuper - 1) / p.msuper, base = m.mc / nsb, extra = m.mc % nsb;
+        const int big = (base + 1) * p.NT;
+        if (rem < extra * big) {
+            const int sb = rem / big;
+            ms = base + 1;
+            mfirst = sb * (base + 1);
+            rem -= sb * big;
+        } else {
+            const int r2 = rem - extra * big, sb = r2 / (base * p.NT);
+            ms = base;
+            mfirst = extra * (base + 1) + sb * base;
+            rem = r2 - sb * base * p.NT;
+        }
+    } else {
+        const int sb = rem / (p.msuper * p.NT);     // m super-block
+        ms = min(p.msuper, m.mc - sb * p.msuper);
+        mfirst = sb * p.msuper;
+        rem -= sb * p.msuper * p.NT;
+    }
     t.g = m.g;
     t.nt = rem / ms;
-    const int mi = sb * kMSuper + rem % ms;
+    const int mi = mfirst + rem % ms;
     const int r0 = p.offsets[m.g], r1 = p.offsets[m.g + 1];
     t.row0 = (int64_t)r0 + (int64_t)mi * BM;
     t.nrows = min(BM, r1 - (int)t.row0);
@@ -137,6 +166,9 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
 // tiles of similar length then share clusters, run in step and reuse each other's operands in L2.
 // GEMM2 was slower that way and keeps group order.
 constexpr int kSortGroups = 4096;
+#ifndef DWDP_SPARSE_ROWS
+#define DWDP_SPARSE_ROWS 0
+#endif
 
 template <int BM>
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int G,
@@ -147,13 +179,52 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
     __shared__ int order_s[kSortGroups];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool sorted = G <= kSortGroups;
-    if (sorted) {
+    if (sorted && DWDP_SPARSE_ROWS == 0) {
         for (int g = tid; g < G; g += 1024) {
             const int n = offsets[g + 1] - offsets[g];
             int rank = 0;
             for (int h = 0; h < G; ++h) {
                 const int m = offsets[h + 1] - offsets[h];
                 rank += (m > n) || (m == n && h < g);
+            }
+            order_s[rank] = g;
+        }
+    } else if (sorted) {
+        // Sparse groups (1 .. DWDP_SPARSE_ROWS rows) stream their weights with little compute; spread
+        // them evenly between the dense groups (each class by size, largest first), so that their weight
+        // streaming runs beside the dense groups' MFMA work instead of after it.  Dense group d of D sits
+        // at key 2 d S, sparse group s of S at (2 s + 1) D.
+        __shared__ int crank_s[kSortGroups];
+        __shared__ int nsparse_s;
+        if (tid == 0) nsparse_s = 0;
+        __syncthreads();
+        auto is_sparse = [&](int n) { return n > 0 && n <= DWDP_SPARSE_ROWS; };
+        for (int g = tid; g < G; g += 1024) {
+            const int n = offsets[g + 1] - offsets[g];
+            const bool sp = is_sparse(n);
+            int rank = 0;
+            for (int h = 0; h < G; ++h) {
+                const int m = offsets[h + 1] - offsets[h];
+                rank += is_sparse(m) == sp && ((m > n) || (m == n && h < g));
+            }
+            crank_s[g] = rank;
+            if (sp) atomicAdd(&nsparse_s, 1);
+        }
+        __syncthreads();
+        const int64_t S = nsparse_s, D = G - nsparse_s;
+        // with one class empty the keys are the class ranks themselves
+        auto key_of = [&](int r, bool sp) -> int64_t {
+            if (S == 0 || D == 0) return r;
+            return sp ? (2 * (int64_t)r + 1) * D : 2 * (int64_t)r * S;
+        };
+        for (int g = tid; g < G; g += 1024) {
+            const bool sp = is_sparse(offsets[g + 1] - offsets[g]);
+            const int64_t key = key_of(crank_s[g], sp);
+            int rank = 0;
+            for (int h = 0; h < G; ++h) {
+                const bool hs = is_sparse(offsets[h + 1] - offsets[h]);
+                const int64_t kh = key_of(crank_s[h], hs);
+                rank += kh < key || (kh == key && !hs && sp);
             }
             order_s[rank] = g;
         }
@@ -372,7 +443,9 @@ struct TileCtx {
 // waves per column group, one per half of the rows (two waves per SIMD): the SIMD switches to the
 // other wave while one waits on LDS or the barrier, and for fp8 one wave's fp32 scale fold runs
 // while the other's MFMAs do.
-constexpr int rowb_of(int BM, bool FP8) { return (FP8 || BM == 32) ? 128 : 64; }
+// 256-row fp8 tiles (compile-time option DWDP_FP8_BM256) take 64-byte K steps: a 128-byte step of 256
+// rows leaves room for only two ring slots
+constexpr int rowb_of(int BM, bool FP8) { return FP8 ? (BM >= 256 ? 64 : 128) : (BM == 32 ? 128 : 64); }
 
 template <int BM, int ROWB, bool FP8>
 struct FragCfg {
@@ -479,7 +552,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     [[maybe_unused]] auto scale_dma = [&](int kt, uint8_t* st) {
-        dma4(reinterpret_cast<const uint8_t*>(gs + kt), st + ABYTES + BBYTES + wave * C::SSTRIDE * 4);
+        dma4(reinterpret_cast<const uint8_t*>(gs + kt * ROWB / kFp8Group), st + ABYTES + BBYTES + wave * C::SSTRIDE * 4);
     };
     auto issue = [&](int kt, int buf) {
         uint8_t* st = smem + buf * STAGE;
@@ -512,10 +585,88 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     // row scale times the weight block's scale.
     // fp8 step kt; the DMA of step ikt into slot ibuf (when iss) is spread over its MFMA blocks, so a
     // wave never waits for the memory pipe to accept its whole batch before its first MFMA
+    // fp8 with 64-byte K steps (256-row tiles): the accumulator is kept in units of the current K block's
+    // scale product c = (row scale) * (weight block scale), so the MFMAs accumulate straight into it.  At
+    // the first half of each 128-wide K block it is multiplied by c_previous / c_current, and after the
+    // last block by c_last: the sum of c_kb * P_kb without a separate partial sum per block.
+    [[maybe_unused]] float cprev[MW][NJ];
+    if constexpr (FP8 && ROWB == 64) {
+#pragma unroll
+        for (int i = 0; i < MW; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) cprev[i][j] = 1.0f;
+    }
     auto compute = [&](int kt, int buf, int ikt, int ibuf, bool iss) {
         const uint8_t* A = smem + buf * STAGE;
         const uint8_t* B = A + ABYTES;
-        if constexpr (FP8) {
+        if constexpr (FP8 && ROWB == 64) {
+            if (!active) {
+                if (iss) issue(ikt, ibuf);
+                return;
+            }
+            const bool first = (kt & 1) == 0;              // first 64-wide half of a 128-wide K block
+            i32x8 bf[NJ], af[MW];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const u32x4 b0 = b_frag(B, j, 0), b1 = b_frag(B, j, 1);
+                bf[j] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                              (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+            }
+#pragma unroll
+            for (int i = 0; i < MW; ++i) {
+                const u32x4 lo = a_frag(A, i, hi * 2), up = a_frag(A, i, hi * 2 + 1);
+                af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2],
+                              (int)up[3]};
+            }
+            float rs[MW][NJ];
+            if (first) {
+                const float* sa_lds = reinterpret_cast<const float*>(B + BBYTES);
+                const int kb = kt / 2;
+#pragma unroll
+                for (int i = 0; i < MW; ++i) {
+                    const int R = rbase + i * 32 + l32;
+                    const float sa = sa_lds[(R / C::RW) * C::SSTRIDE + R % C::RW];
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const float c = sa * s_bscale[(wave * NJ + j) * 64 + kb];
+                        rs[i][j] = cprev[i][j] * __builtin_amdgcn_rcpf(c);     // c > 0: scales are amax/448 or 1
+                        cprev[i][j] = c;
+                    }
+                }
+            }
+            constexpr int NB = MW * NJ, QB = (PER + NB - 1) / NB;   // DMA instructions per block
+            auto rescale = [&](int b) {
+                const int i = b / NJ, j = b % NJ;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] *= rs[i][j];
+            };
+            auto mfma = [&](int b) {
+                const int i = b / NJ, j = b % NJ;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0, 127,
+                                                                            0, 127);
+            };
+            if (first) {
+                // block b's rescale runs under block b-1's MFMA
+                rescale(0);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    mfma(b);
+                    if (iss) issue_part(ikt, ibuf, b * QB, (b + 1) * QB);
+                    if (b + 1 < NB) rescale(b + 1);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // block b's MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x020, QB, 0);   // part of the next DMA batch
+                    if (b + 1 < NB) __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);   // block b+1's rescale
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    mfma(b);
+                    if (iss) issue_part(ikt, ibuf, b * QB, (b + 1) * QB);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, QB, 0);
+                }
+            }
+        } else if constexpr (FP8) {
             if (!active) {
                 if (iss) issue(ikt, ibuf);
                 return;
@@ -714,6 +865,16 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     }
 
     // ---------------------------------------------------------------- epilogue
+    if constexpr (FP8 && ROWB == 64) {
+        if (active) {
+#pragma unroll
+            for (int i = 0; i < MW; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] *= cprev[i][j];
+        }
+    }
     if constexpr (KIND == kGemm1) {
         if constexpr (!FP8) {
             // Blocks are transposed (lane l32 holds row rbase + 32 i + l32, element r holds A column
@@ -1028,9 +1189,13 @@ int choose_bm(int dtype, int64_t rows, int groups) {
     if (dtype == DWDP_F32) return kBmF32;
     const int64_t mean = rows / groups;
     const int bm = mean >= 192 ? 256 : mean >= 96 ? 128 : mean >= 40 ? 64 : 32;
-    // fp8 stays at 128 rows: a 256-row tile only fits the LDS ring with 64-wide K steps, which folds
-    // every partial sum twice per scale block (measured 11.7 vs 9.6 ms for GEMM1 at 16K tokens)
+#ifdef DWDP_FP8_BM256
+    return bm;
+#else
+    // fp8 stays at 128 rows by default: 256-row fp8 tiles (64-byte K steps, the accumulator rescaled at
+    // every 128-wide K block) measured GEMM1 5.96 vs 5.60 ms and GEMM2 3.43 vs 3.49 ms at 16K tokens
     return dtype == DWDP_FP8_E4M3 && bm > 128 ? 128 : bm;
+#endif
 }
 
 template <int BM>
@@ -1066,7 +1231,12 @@ template <int BM>
 void launch_ffn(bool g1, bool g2, bool fp8_path, const int32_t* offsets, int G, const GemmParams& p1,
                 const GemmParams& p2, MTile* mt_group, MTile* mt_size, int64_t maxm, hipStream_t st) {
     if (g1) launch_schedule<BM>(offsets, G, const_cast<int32_t*>(p1.mprefix), mt_group, mt_size, st);
-    if constexpr (BM <= 128) {
+#ifdef DWDP_FP8_BM256
+    constexpr bool fp8_tiles = true;
+#else
+    constexpr bool fp8_tiles = BM <= 128;
+#endif
+    if constexpr (fp8_tiles) {
         if (fp8_path) {
             if (g1) launch_dma<BM, kGemm1, true>(p1, maxm * p1.NT, st);
             if (g2) launch_dma<BM, kGemm2, true>(p2, maxm * p2.NT, st);
@@ -1162,6 +1332,7 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     p1.K = H;
     p1.I = I;
     p1.NT = w_dtype == DWDP_F32 ? I / (kBnF32 / 2) : I / (kBnDma / 2);
+    p1.msuper = w_dtype == DWDP_FP8_E4M3 ? DWDP_MSUPER_FP8 : DWDP_MSUPER_BF16;
     p1.out = base + L.a;
     p1.out_scale = reinterpret_cast<float*>(base + L.a_scale);
 
@@ -1186,7 +1357,7 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
         if (g2) launch_f32<kGemm2>(p2, maxm * p2.NT, st);
     } else {
         const bool fp8 = w_dtype == DWDP_FP8_E4M3;
-        if (bm == 256) launch_ffn<256>(g1, g2, false, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
+        if (bm == 256) launch_ffn<256>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
         else if (bm == 128) launch_ffn<128>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
         else if (bm == 64) launch_ffn<64>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
         else launch_ffn<32>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);

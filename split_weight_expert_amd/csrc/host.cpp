@@ -126,7 +126,14 @@ extern "C" {
 
 const char* dwdp_last_error(void) { return g_last_error.c_str(); }
 
-const char* dwdp_version(void) { return "dwdp-mi355x 0.1 (gfx950)"; }
+// The compile-time kernel options this build was made with are listed after the architecture.
+const char* dwdp_version(void) {
+#ifdef DWDP_FP8_BM256
+    return "dwdp-mi355x 0.2 (gfx950) fp8-bm256";
+#else
+    return "dwdp-mi355x 0.2 (gfx950)";
+#endif
+}
 
 size_t dwdp_expert_record_bytes(int H, int I, int w_dtype) {
     if (H <= 0 || I <= 0 || elem_bytes(w_dtype) == 0) return 0;

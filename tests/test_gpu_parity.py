@@ -228,6 +228,8 @@ FFN_CASES = {
     "bf16": ("prefill8k_bf16", dict(T=200, H=512, I=256, E=8, k=2, n_local=4)),
     "fp8": ("prefill16k_fp8", dict(T=200, H=512, I=256, E=8, k=2, n_local=4)),
     "fp8_bm128": ("prefill16k_fp8", dict(T=300, H=512, I=256, E=4, k=2, n_local=2)),
+    # 256-row fp8 tiles when built with DWDP_FP8_BM256 (128-row tiles otherwise)
+    "fp8_bm256": ("prefill16k_fp8", dict(T=650, H=768, I=384, E=4, k=2, n_local=2)),
 }
 
 
@@ -238,7 +240,7 @@ def skew_bias(E):
     return b
 
 
-@pytest.mark.parametrize("case", ["f32", "bf16", "fp8", "bf16_bm128", "bf16_bm256", "fp8_bm128"])
+@pytest.mark.parametrize("case", ["f32", "bf16", "fp8", "bf16_bm128", "bf16_bm256", "fp8_bm128", "fp8_bm256"])
 def test_grouped_ffn_parity(case):
     from split_weight_expert_amd import MoEBlock
     name, kw = FFN_CASES[case]
@@ -257,7 +259,8 @@ def test_grouped_ffn_parity(case):
     ps = bb.perm_src.cpu().numpy()
     counts = np.diff(off)
     assert counts[0] > 128 and counts[cfg.E - 1] == 0
-    assert cfg.rows // (cfg.E + cfg.shared) >= {"bf16_bm128": 96, "bf16_bm256": 192, "fp8_bm128": 96}.get(case, 0)
+    assert cfg.rows // (cfg.E + cfg.shared) >= {"bf16_bm128": 96, "bf16_bm256": 192, "fp8_bm128": 96,
+                                                 "fp8_bm256": 192}.get(case, 0)
     y_perm = to_np(bb.y_perm).astype(np.float64)
     ws = list(h.experts) + ([h.shared] if h.shared is not None else [])
     ref = np.zeros_like(y_perm)
@@ -643,14 +646,18 @@ def test_permute_and_combine_drop_out_of_range_indices():
 # --------------------------------------------------------------------------------------- deep K, every tail
 
 # Group sizes chosen so that the last m-tile of the groups holds every row count the kernels have a
-# variant for.  bf16 runs 256-row tiles (mean rows per group >= 192): tails of 20, 50, 80, 120, 180,
-# 250 and 256 rows (1..8 active 32-row blocks, spread over the two 128-row halves).  fp8 runs 128-row
-# tiles: tails of 20, 50, 80, 120 and 128 rows.  An empty group is included.  K = 2048 (GEMM1) and
-# 1024 (GEMM2) are deep enough for the steady-state loops of both DMA rings (bf16: 64 and 32 K steps
-# against NS + P = 8; fp8: 16 and 8 against NS + P - 1 = 4).
+# variant for.  With a mean of 192 or more rows per group bf16 runs 256-row tiles: tails of 20, 50, 80,
+# 120, 144, 180, 204, 250 and 256 rows (1..8 active 32-row blocks, spread over the two 128-row halves);
+# fp8 runs 128-row tiles there too unless the library is built with DWDP_FP8_BM256, which gives it
+# 256-row tiles.  The fp8_bm128 case (mean rows per group 96..191) runs 128-row fp8 tiles: tails of 20,
+# 50, 80, 120 and 128 rows.  An empty group is included.  K = 2048 (GEMM1) and 1024 (GEMM2) are deep
+# enough for the steady-state loops of every DMA ring (bf16 and 256-row fp8 tiles step 64 bytes of K:
+# 64 and 32 steps for bf16 and 32 and 16 for fp8, against NS + P = 8 and 7; 128-row fp8 tiles step
+# 128 bytes: 16 and 8 steps against NS + P - 1 = 4).
 TAIL_CASES = {
-    "bf16": dict(H=2048, I=1024, sizes=[276, 306, 336, 376, 436, 506, 512, 0, 20]),
-    "fp8": dict(H=2048, I=1024, sizes=[148, 178, 208, 248, 256, 0, 600, 20]),
+    "bf16": dict(H=2048, I=1024, sizes=[276, 306, 336, 376, 400, 436, 460, 506, 512, 0, 20]),
+    "fp8": dict(H=2048, I=1024, sizes=[276, 306, 336, 376, 400, 436, 460, 506, 512, 0, 20]),
+    "fp8_bm128": dict(H=2048, I=1024, sizes=[148, 178, 208, 248, 20, 36, 40, 70, 100, 0, 60, 90]),
 }
 
 
@@ -661,18 +668,19 @@ def normal_expert(rng, H, I):
             rng.normal(0, I ** -0.5, size=(H, I)).astype(np.float32))
 
 
-@pytest.mark.parametrize("dt", ["bf16", "fp8"])
-def test_grouped_ffn_every_tail_variant_deep_k(dt):
+@pytest.mark.parametrize("case", ["bf16", "fp8", "fp8_bm128"])
+def test_grouped_ffn_every_tail_variant_deep_k(case):
     """Every y_perm row of a grouped FFN whose groups end on every tile-tail variant, at K large enough
     for the steady-state DMA ring loops, against the oracle's expert FFN; inputs from numpy's normal
     generator (unbounded tails, which set the fp8 group maxima)."""
     from split_weight_expert_amd import ExpertStore, api
     from split_weight_expert_amd.moe import DTYPES
-    c = TAIL_CASES[dt]
+    c = TAIL_CASES[case]
+    dt = case.split("_")[0]
     H, I, sizes = c["H"], c["I"], c["sizes"]
     E, k, S = len(sizes), 1, 1
     T = int(sum(sizes))
-    rng = np.random.default_rng(123 if dt == "bf16" else 321)
+    rng = np.random.default_rng({"bf16": 123, "fp8": 321, "fp8_bm128": 231}[case])
     idx = np.repeat(np.arange(E), sizes).astype(np.int32)[rng.permutation(T)].reshape(T, 1)
     x = rng.normal(0, 1, size=(T, H)).astype(np.float32)
     x[7, 5] = 9.0                                              # an outlier sets one group's scale
@@ -731,11 +739,16 @@ def test_grouped_ffn_every_tail_variant_deep_k(dt):
     ref = np.concatenate([parts[g][0]["Y"] for g in sorted(parts)])
     rms = np.sqrt((ref ** 2).mean())
     stats = {}
+    clean_mx, flipped = 0.0, 0
     for g, (pt, w2) in parts.items():
         r0, r1 = o[g], o[g + 1]
-        check_fp8_rows(y[r0:r1], codes[r0:r1], scales[r0:r1], pt, w2, rms, f"fp8 tails group {g}", stats)
+        # rows whose A codes equal the oracle's meet the fp8 maximum; rows with re-quantisation flips are
+        # bounded by the flips' effect (check_fp8_rows)
+        nf, cm = check_fp8_rows(y[r0:r1], codes[r0:r1], scales[r0:r1], pt, w2, rms, f"{case} tails group {g}", stats)
+        clean_mx, flipped = max(clean_mx, cm), flipped + nf
     mx, mn = rel_err(y, ref)
-    assert mx <= TOL["fp8"]["max"] and mn <= TOL["fp8"]["mean"]
-    print(f"[tails fp8] rows {rows} max rel {mx:.2e} mean rel {mn:.2e}; A codes {stats['codes']}, "
+    assert mn <= TOL["fp8"]["mean"], f"mean rel {mn:.2e}"
+    print(f"[tails {case}] rows {rows} max rel {mx:.2e} (rows without flips {clean_mx:.2e}; {flipped} rows with "
+          f"flips) mean rel {mn:.2e}; A codes {stats['codes']}, "
           f"flips {stats['flips']} ({stats['flips'] / stats['codes']:.2e}), worst flip "
           f"{stats['worst_window']:.3f} windows, scales within {stats['scale_rel_max']:.1e}", flush=True)
