@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-merge", action="store_true", help="skip the merge-copy ablation")
     ap.add_argument("--pipeline-layers", type=int, default=0,
                     help="also run this many layers back to back with ping-pong prefetch slots")
+    ap.add_argument("--slot-sets", type=int, default=2,
+                    help="prefetch slot sets of the pipeline measurement (2 = the pages' double buffer)")
     ap.add_argument("--copy-workgroups", type=int, default=48)
     ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy", "sdma"],
                     help="engine of the pipeline and smi measurements")
@@ -272,7 +274,8 @@ def run_workload(cfg, args, steps, warmup, main):
     want_prefetch = not args.no_prefetch and cfg.n_prefetch > 0
     log(f"setting up {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} dtype={cfg.dtype}")
     t0 = time.perf_counter()
-    layer = DeviceLayer(cfg, dev, sources=want_prefetch)
+    layer = DeviceLayer(cfg, dev, sources=want_prefetch,
+                        slot_sets=max(2, args.slot_sets) if main and args.pipeline_layers > 0 else 2)
     log(f"layer resident in {time.perf_counter() - t0:.1f} s")
     block = layer.block()
     table = layer.table(1)
@@ -548,8 +551,9 @@ def measure_pipeline(layer, block, step, args, cfg, pf):
     engine = {"kernel": api.COPY_KERNEL, "hipmemcpy": api.COPY_HIPMEMCPY, "sdma": api.COPY_SDMA}[args.copy_engine]
     chunk = int(args.chunk_mib * (1 << 20)) if args.chunk_mib else cfg.chunk_bytes
     comp = torch.cuda.current_stream()
+    N = max(2, args.slot_sets)
     pipe = DWDPPipeline(cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, cfg.dtype, cfg.n_local, layer.device,
-                        slot_sets=[layer.store.buffers[1], layer.store.buffers[2]], chunk_bytes=chunk, engine=engine,
+                        slot_sets=layer.store.buffers[1:1 + N], chunk_bytes=chunk, engine=engine,
                         max_workgroups=args.copy_workgroups)
     pipe.block = block
     lw = LayerWeights(layer.w_router, layer.bias, layer.store.buffers[0], layer.sources)
@@ -577,11 +581,14 @@ def measure_pipeline(layer, block, step, args, cfg, pf):
     tp = pf["copy_ms"]
     # both slot sets now hold the sources' bytes: spot-check one record of each
     per = cfg.n_prefetch // cfg.n_sources
-    ok = all(bool(torch.equal(layer.store.record(k, per + 1), layer.src_store.record(1, 1))) for k in (1, 2))
-    return dict(layers=L, ms_per_layer=t / L, compute_ms_per_layer=tc, copy_ms_alone=tp, max_tc_tp=max(tc, tp),
-                layer_over_max=(t / L) / max(tc, tp), record_check=ok,
-                note="DWDPPipeline over the MoE block only (no attention); the pull of layer l+1 overlaps layer l; "
-                     "timed from layer 0's block to the end of the last layer")
+    ok = all(bool(torch.equal(layer.store.record(k, per + 1), layer.src_store.record(1, 1))) for k in range(1, N + 1))
+    model = max(tc, tp / (N - 1))
+    return dict(layers=L, slot_sets=N, engine=args.copy_engine, chunk_bytes=chunk, ms_per_layer=t / L,
+                compute_ms_per_layer=tc, copy_ms_alone=tp, max_tc_tp=max(tc, tp), model_ms=model,
+                layer_over_model=(t / L) / model, layer_over_compute=(t / L) / tc, record_check=ok,
+                note="DWDPPipeline over the MoE block only (no attention); with N slot sets the pull of layer "
+                     "l+N-1 overlaps layers l..l+N-2; model = max(compute, copy / (N-1)); timed from layer 0's "
+                     "block to the end of the last layer")
 
 
 def measure_prefetch(layer, block, step, args, cfg, ms_block, engine_name):
@@ -652,9 +659,11 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block, engine_name):
         tb = start.elapsed_time(b_end)
         return tb, (start.elapsed_time(c_end) if with_copy else None)
 
-    t_alone, t_blk, t_cp = [], [], []
-    for _ in range(reps):            # interleaved, so both see the same clock and thermal history
-        t_alone.append(single(False)[0])
+    # the block alone first (each from an idle GPU, as in the copy's leg, but not right after a copy: a
+    # copy that runs on alone leaves the block's operands evicted from the caches), then beside the copy
+    t_alone = [single(False)[0] for _ in range(reps)]
+    t_blk, t_cp = [], []
+    for _ in range(reps):
         tb, tc = single(True)
         t_blk.append(tb)
         t_cp.append(tc)

@@ -225,13 +225,16 @@ class LayerWeights:
 
 
 class DWDPPipeline:
-    """Layer-ahead prefetch over a double-buffered slot area (DWDP paper summary §2, §4.3.2).
+    """Layer-ahead prefetch over a ring of N >= 2 prefetch slot sets (DWDP paper summary §2, §4.3.2).
 
-    While layer l computes on the compute stream from slot set l % 2, a copy stream pulls layer l+1's
-    non-local experts into slot set (l + 1) % 2 in fixed-size slices, round-robin over the sources.
-    Two hazards are ordered with events: layer l waits for the copy that filled its slot set, and a
-    copy into a slot set waits for the layer that last read it.  The layer time is then
-    max(compute, copy) (the layer-wise model of the pages, §3), not their sum.
+    With the pages' double buffer (N = 2), while layer l computes on the compute stream from slot set
+    l % 2, a copy stream pulls layer l+1's non-local experts into slot set (l + 1) % 2 in fixed-size
+    slices, round-robin over the sources.  With N slot sets the pull of layer l + N - 1 starts as soon
+    as layer l - 1 has released its slot set, so each pull may spread over N - 1 layers of compute
+    (one GPU's 288 GB of HBM holds several fp8 slot sets of a DeepSeek-R1 layer, 8.5 GB each).  Two
+    hazards are ordered with events: layer l waits for the copy that filled its slot set, and a copy
+    into a slot set waits for the layer that last read it.  The layer time is then max(compute,
+    copy / (N - 1)) (the layer-wise model of the pages, §3, for N = 2), not their sum.
 
     The block reads each layer's weights through a pointer table over two buffers -- the layer's
     resident records and the current slot set -- so nothing is merged.  Only the MoE blocks run here
@@ -246,15 +249,16 @@ class DWDPPipeline:
         self.device = torch.device(device)
         self.rec = api.expert_record_bytes(H, I, self.w_dtype)
         self.n_pre = E - n_local
-        if slot_sets is None:
+        if slot_sets is None or isinstance(slot_sets, int):
+            n = 2 if slot_sets is None else slot_sets
             slot_sets = [torch.empty(max(self.n_pre, 1) * self.rec, dtype=torch.uint8, device=self.device)
-                         for _ in range(2)]
-        assert len(slot_sets) == 2 and all(t.numel() >= self.n_pre * self.rec for t in slot_sets)
-        self.slot_sets = slot_sets
+                         for _ in range(n)]
+        assert len(slot_sets) >= 2 and all(t.numel() >= self.n_pre * self.rec for t in slot_sets)
+        self.slot_sets = list(slot_sets)
         self.chunk_bytes, self.engine, self.max_workgroups = chunk_bytes, engine, max_workgroups
         self.block = MoEBlock(H, I, E, k, shared, dtype, self.device)
         self.copy_stream = torch.cuda.Stream(self.device)
-        self._last_read = [None, None]      # event of the last layer that read each slot set
+        self._last_read = [None] * len(self.slot_sets)   # event of the last layer that read each slot set
         self._tables = {}
 
     def placement(self):
@@ -303,7 +307,8 @@ class DWDPPipeline:
         if outputs is None:
             bufs = [torch.empty(T, self.H, dtype=x.dtype, device=self.device) for _ in range(min(L, 2))]
             outputs = [bufs[l % 2] for l in range(L)]
-        copy_done = [torch.cuda.Event(), torch.cuda.Event()]
+        N = len(self.slot_sets)
+        copy_done = [torch.cuda.Event() for _ in range(N)]
         # the copy stream must not start before everything already enqueued on the compute stream
         # that produced the sources or this call's input
         start = torch.cuda.Event()
@@ -316,12 +321,11 @@ class DWDPPipeline:
                     before_copy(l)
             self.prefetch(layers[l], s, wait=self._last_read[s], done=copy_done[s])
 
-        if L:
-            pull(0, 0)
+        # layers 0 .. N-2 into slot sets 0 .. N-2 (each waits for its set's last reader of an earlier call)
+        for l in range(min(L, N - 1)):
+            pull(l, l)
         for l in range(L):
-            s = l % 2
-            if l + 1 < L:
-                pull(l + 1, 1 - s)
+            s = l % N
             comp.wait_event(copy_done[s])
             if before_compute is not None:
                 before_compute(l)
@@ -331,6 +335,11 @@ class DWDPPipeline:
                 after_layer(l, b)
             ev = torch.cuda.Event()
             ev.record(comp)
+            # the pull into slot set (l - 1) % N, released by layer l - 1 (or by an earlier call), is
+            # enqueued after layer l's block: an engine whose enqueue blocks the host (the DMA engines
+            # when their queue is full) then does not hold back the block's launches
+            if l + N - 1 < L:
+                pull(l + N - 1, (l + N - 1) % N)
             self._last_read[s] = ev
             if chain:
                 x = outputs[l]

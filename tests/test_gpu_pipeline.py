@@ -1,8 +1,9 @@
 """The layer-ahead prefetch pipeline (DWDPPipeline) against the per-layer oracle, with delays injected.
 
 L = 4 distinct seeded layers, each with its own resident records and its own stand-in source
-allocations for its non-local experts, run back to back: layer l reads prefetch slot set l % 2 while
-the copy stream fills the other set with layer l+1's experts (DWDP paper summary §2; §4.3.2 slices).
+allocations for its non-local experts, run back to back: layer l reads prefetch slot set l % N while
+the copy stream fills the other sets with the next layers' experts (N = 2, the pages' double buffer,
+DWDP paper summary §2; §4.3.2 slices; and N = 3).
 Delays are injected at enqueue time with torch.cuda._sleep on the copy stream (each pull starts late,
 so a layer that did not wait for its copy would read the weights of layer l-2 left in its slot set)
 and on the compute stream (each layer runs late, so a pull that did not wait for the last reader would
@@ -77,16 +78,16 @@ def build_layers(cfg):
     return host, dev, stores
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("engine", [0, 1])
-def test_pipeline_with_delays_matches_the_per_layer_oracle(dt, engine):
+@pytest.mark.parametrize("dt,engine,n_sets", [("f32", 0, 2), ("f32", 1, 2), ("bf16", 0, 2), ("bf16", 1, 2),
+                                               ("bf16", 1, 3), ("f32", 0, 3)])
+def test_pipeline_with_delays_matches_the_per_layer_oracle(dt, engine, n_sets):
     from split_weight_expert_amd import DWDPPipeline
     name, kw = CASES[dt]
     cfg = shrink(synth.get_config(name), **kw)
     host, layers, stores = build_layers(cfg)
     rec = stores[0].rec
     # small slices, so that a pull is many round-robin slices
-    pipe = DWDPPipeline(cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, cfg.dtype, cfg.n_local, DEV,
+    pipe = DWDPPipeline(cfg.H, cfg.I, cfg.E, cfg.k, cfg.shared, cfg.dtype, cfg.n_local, DEV, slot_sets=n_sets,
                         chunk_bytes=max(4096, rec // 3 // 16 * 16), engine=engine, max_workgroups=3)
     adt = torch.float32 if dt == "f32" else torch.bfloat16
     x0 = torch.from_numpy(synth.tokens(cfg)).to(DEV, adt)
@@ -111,6 +112,6 @@ def test_pipeline_with_delays_matches_the_per_layer_oracle(dt, engine):
             ref = omoe.moe_layer(x_np, h["wr"], h["b"], cfg.k, lambda e, h=h: h["experts"][e],
                                  (lambda h=h: h["shared"]) if cfg.shared else None, precision=dt,
                                  routing=(lg, gi, omoe.gate_weights(lg, gi)))
-            assert_close(to_np(outs[l]), ref["y"], dt, f"call {call} layer {l} ({dt}, engine {engine})")
+            assert_close(to_np(outs[l]), ref["y"], dt, f"call {call} layer {l} ({dt}, engine {engine}, {n_sets} sets)")
             xin = outs[l]
     del stores
