@@ -402,9 +402,19 @@ __global__ __launch_bounds__(WM * WN * 64) void router_mfma_kernel(GemmParams p)
 //     wait; its LDS reads are interleaved one by one with the MFMAs.  fp8 keeps P = NS - 1.
 //   * Activation rows are swizzled in LDS (aslot) so that the 16 lanes one ds_read_b128 cycle
 //     serves hit 16 distinct 16-byte slots of the 256-byte bank window.
+//   * Cache policy of the operand loads (compile-time options, 0 = default): DWDP_WEIGHT_CPOL for the
+//     weight fragments and DWDP_ACT_CPOL for the activation rows, as the instruction's cache-policy
+//     bits (2 = non-temporal: the lines are streamed, not kept for reuse).
+#ifndef DWDP_WEIGHT_CPOL
+#define DWDP_WEIGHT_CPOL 0
+#endif
+#ifndef DWDP_ACT_CPOL
+#define DWDP_ACT_CPOL 0
+#endif
+template <int CPOL = 0>
 __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, CPOL);
 #endif
 }
 
@@ -557,9 +567,9 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     auto issue = [&](int kt, int buf) {
         uint8_t* st = smem + buf * STAGE;
 #pragma unroll
-        for (int i = 0; i < AI; ++i) dma16(ga[i] + (size_t)kt * ROWB, st + (wave * AI + i) * 1024);
+        for (int i = 0; i < AI; ++i) dma16<DWDP_ACT_CPOL>(ga[i] + (size_t)kt * ROWB, st + (wave * AI + i) * 1024);
 #pragma unroll
-        for (int q = 0; q < BIW; ++q) dma16(gb[q] + (size_t)kt * BF * 1024, st + lb[q]);
+        for (int q = 0; q < BIW; ++q) dma16<DWDP_WEIGHT_CPOL>(gb[q] + (size_t)kt * BF * 1024, st + lb[q]);
         if constexpr (FP8) scale_dma(kt, st);
     };
     // DMA instructions q0 .. q1-1 of a step's PER (activation rows, weight fragments, row scales)
@@ -568,8 +578,8 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             if (q < q0 || q >= q1) continue;
-            if (q < AI) dma16(ga[q] + (size_t)kt * ROWB, st + (wave * AI + q) * 1024);
-            else if (q < AI + BIW) dma16(gb[q - AI] + (size_t)kt * BF * 1024, st + lb[q - AI]);
+            if (q < AI) dma16<DWDP_ACT_CPOL>(ga[q] + (size_t)kt * ROWB, st + (wave * AI + q) * 1024);
+            else if (q < AI + BIW) dma16<DWDP_WEIGHT_CPOL>(gb[q - AI] + (size_t)kt * BF * 1024, st + lb[q - AI]);
             else if constexpr (FP8) scale_dma(kt, st);
         }
     };

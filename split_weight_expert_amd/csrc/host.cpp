@@ -72,8 +72,7 @@ size_t ffn_ws_bytes(int64_t rows, int groups, int H, int I, int dtype) {
 }
 
 size_t permute_ws_bytes(int64_t T, int k, int E) {
-    (void)T;
-    (void)k;
+    if (E <= kHistMaxE) return align256((size_t)hist_chunks(T * k) * (size_t)E * 4);   // [chunks][E]
     return align256((size_t)E * kPermuteWaves * 4 * 2);
 }
 
@@ -127,12 +126,32 @@ extern "C" {
 const char* dwdp_last_error(void) { return g_last_error.c_str(); }
 
 // The compile-time kernel options this build was made with are listed after the architecture.
+#define DWDP_STR2(x) #x
+#define DWDP_STR(x) DWDP_STR2(x)
 const char* dwdp_version(void) {
+    return "dwdp-mi355x 0.2 (gfx950)"
 #ifdef DWDP_FP8_BM256
-    return "dwdp-mi355x 0.2 (gfx950) fp8-bm256";
-#else
-    return "dwdp-mi355x 0.2 (gfx950)";
+           " fp8-bm256"
 #endif
+#ifdef DWDP_MSUPER_BF16
+           " msuper-bf16=" DWDP_STR(DWDP_MSUPER_BF16)
+#endif
+#ifdef DWDP_MSUPER_FP8
+           " msuper-fp8=" DWDP_STR(DWDP_MSUPER_FP8)
+#endif
+#ifdef DWDP_MSUPER_BALANCED
+           " msuper-balanced=" DWDP_STR(DWDP_MSUPER_BALANCED)
+#endif
+#ifdef DWDP_SPARSE_ROWS
+           " sparse-rows=" DWDP_STR(DWDP_SPARSE_ROWS)
+#endif
+#ifdef DWDP_WEIGHT_CPOL
+           " weight-cpol=" DWDP_STR(DWDP_WEIGHT_CPOL)
+#endif
+#ifdef DWDP_ACT_CPOL
+           " act-cpol=" DWDP_STR(DWDP_ACT_CPOL)
+#endif
+        ;
 }
 
 size_t dwdp_expert_record_bytes(int H, int I, int w_dtype) {

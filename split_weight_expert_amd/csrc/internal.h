@@ -12,7 +12,17 @@ namespace dwdp {
 constexpr int kMaxCopySources = 64;
 constexpr int kBmMin = 32;             // smallest expert-GEMM tile height (sizes the m-tile tables)
 constexpr size_t kMTileBytes = 16;     // one entry of an m-tile table
-constexpr int kPermuteWaves = 16;      // waves per count / scatter workgroup of the permutation
+constexpr int kPermuteWaves = 16;      // waves per count / scatter workgroup of the permutation (E > kHistMaxE)
+// Permutation by chunk histograms (E <= kHistMaxE): the T*k entries are cut into chunks of
+// hist_chunk(N) consecutive entries, one wave each, so that there are at most kHistMaxChunks of them.
+constexpr int kHistMaxE = 4096;
+constexpr int64_t kHistMaxChunks = 1024;
+inline int64_t hist_chunk(int64_t N) {
+    const int64_t per = (N + kHistMaxChunks - 1) / kHistMaxChunks;
+    const int64_t c = (per + 63) / 64 * 64;
+    return c < 1024 ? 1024 : c;
+}
+inline int64_t hist_chunks(int64_t N) { return (N + hist_chunk(N) - 1) / hist_chunk(N); }
 
 // Grouped-FFN workspace: A [rows, I] in the activation type (+ its fp8 scales [rows, I/128]), the
 // m-tile prefix [G+1] and two m-tile tables, each part 256-byte aligned; the tables are sized for

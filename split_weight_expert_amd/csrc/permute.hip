@@ -2,16 +2,29 @@
 // that is stable in the flattened index t*k+j -- and the row gather that
 // builds x_perm, optionally quantising each row to fp8 E4M3 per 128 columns.
 //
-//   count    one workgroup per expert, 16 waves; wave w scans a fixed slice of
-//            topk_idx, each lane 16 consecutive entries, and counts matches
-//   offsets  one workgroup: per-expert totals, their exclusive scan (the group
-//            row offsets) and the base row of every (expert, wave) slice
+// Up to kHistMaxE experts the sort works on chunk histograms, O(T*k) work:
+//   chunk_count    one wave per chunk of consecutive entries: its expert
+//                  histogram in LDS, written out as row c of [chunks][E]
+//   chunk_offsets  one workgroup: per-expert totals, their exclusive scan (the
+//                  group row offsets), and the histogram rewritten in place as
+//                  the first row of every (chunk, expert) pair
+//   chunk_scatter  each wave walks its chunk again, 64 entries at a time; the
+//                  lanes that hold the same expert find each other with one
+//                  ballot per bit of the expert index, so an entry's row is its
+//                  (chunk, expert) base + entries of that expert before it in
+//                  the chunk, which keeps the t*k+j order
+// Above kHistMaxE (the histograms would not fit in LDS) one workgroup per
+// expert scans all entries, O(E*T*k):
+//   count    16 waves; wave w scans a fixed slice of topk_idx, each lane 16
+//            consecutive entries, and counts matches
+//   offsets  one workgroup: per-expert totals, their exclusive scan and the base
+//            row of every (expert, wave) slice
 //   scatter  the count walk again, now with a 64-lane prefix scan of the
 //            per-lane match counts: rank = slice base + lanes before + matches
-//            before inside the lane, which keeps the t*k+j order
+//            before inside the lane
 //   gather   one workgroup per x_perm row: bitwise row copy, or per-row fp8
 //            quantisation (scale = amax/448 over 128 columns, code = E4M3(v/s))
-// No atomics are involved, so every output is bitwise reproducible.
+// Every output is bitwise reproducible: the only atomics add integers in LDS.
 #include "common.h"
 #include "internal.h"
 
@@ -149,6 +162,152 @@ __global__ __launch_bounds__(1024) void scatter_kernel(const int32_t* __restrict
     }
 }
 
+// ---------------------------------------------------------------- chunk histograms (E <= kHistMaxE)
+constexpr int kHistWaves = 4;   // chunks (waves) per workgroup
+
+// Row c of hist [chunks][E]: how many entries of chunk c name each expert (entries outside [0, E)
+// are dropped and counted nowhere).
+__global__ __launch_bounds__(256) void chunk_count_kernel(const int32_t* __restrict__ idx, int64_t N, int E,
+                                                          int64_t chunk, int64_t C, int32_t* __restrict__ hist) {
+    __shared__ int32_t cnt_s[kHistWaves * kHistMaxE];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t c = (int64_t)blockIdx.x * kHistWaves + w;
+    int32_t* cnt = cnt_s + w * E;
+    for (int e = lane; e < E; e += 64) cnt[e] = 0;
+    __syncthreads();
+    if (c < C) {
+        const int64_t lo = c * chunk, hi = min(N, lo + chunk);
+        for (int64_t i = lo + lane; i < hi; i += 64) {
+            const int v = idx[i];
+            if (v >= 0 && v < E) atomicAdd(&cnt[v], 1);
+        }
+    }
+    __syncthreads();
+    if (c < C)
+        for (int e = lane; e < E; e += 64) hist[c * E + e] = cnt[e];
+}
+
+// offsets[e] = exclusive scan of the expert totals; hist[c][e] becomes the first row of chunk c's
+// entries of expert e (offsets[e] + the entries of e in chunks before c).  Experts are taken EB at a
+// time, and the chunks of each expert are split into P = 1024 / EB segments with a thread each, so that
+// a thread's loads are a few batches of independent ones rather than one chain over all chunks.
+constexpr int kOffBatch = 16;
+__global__ __launch_bounds__(1024) void chunk_offsets_kernel(int32_t* __restrict__ hist, int64_t C, int E, int shared,
+                                                             int64_t T, int64_t R, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ perm_src) {
+    __shared__ int part_s[1024];     // segment sums, [segment][expert of the block]
+    __shared__ int excl_s[1024];     // offsets of the block's experts
+    __shared__ int wsum[16];
+    __shared__ int carry_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int P = E >= 1024 ? 1 : 1024 / E, EB = 1024 / P;
+    const int sg = tid / EB, el = tid % EB;
+    const int64_t SC = (C + P - 1) / P;                     // chunks per segment
+    const int64_t c_lo = min(C, (int64_t)sg * SC), c_hi = min(C, c_lo + SC);
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int base = 0; base < E; base += EB) {
+        const int e = base + el;
+        const bool mine = sg < P && e < E;
+        int sum = 0;
+        if (mine) {
+            for (int64_t c0 = c_lo; c0 < c_hi; c0 += kOffBatch) {
+                int h[kOffBatch];
+#pragma unroll
+                for (int q = 0; q < kOffBatch; ++q) h[q] = c0 + q < c_hi ? hist[(c0 + q) * E + e] : 0;
+#pragma unroll
+                for (int q = 0; q < kOffBatch; ++q) sum += h[q];
+            }
+        }
+        part_s[tid] = sum;
+        __syncthreads();
+        int tot = 0;                                       // thread el < EB of segment 0 holds expert el's total
+        if (sg == 0 && e < E)
+            for (int q = 0; q < P; ++q) tot += part_s[q * EB + el];
+        const int incl = wave_incl_scan(tot, lane);
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int before = carry_s;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        if (sg == 0) {
+            const int excl = before + incl - tot;
+            excl_s[el] = excl;
+            if (e < E) offsets[e] = excl;
+        }
+        __syncthreads();
+        if (mine) {
+            int run = excl_s[el];
+            for (int q = 0; q < sg; ++q) run += part_s[q * EB + el];
+            for (int64_t c0 = c_lo; c0 < c_hi; c0 += kOffBatch) {
+                int h[kOffBatch];
+#pragma unroll
+                for (int q = 0; q < kOffBatch; ++q) h[q] = c0 + q < c_hi ? hist[(c0 + q) * E + e] : 0;
+#pragma unroll
+                for (int q = 0; q < kOffBatch; ++q) {
+                    if (c0 + q < c_hi) hist[(c0 + q) * E + e] = run;
+                    run += h[q];
+                }
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int total = 0;
+            for (int w = 0; w < 16; ++w) total += wsum[w];
+            carry_s += total;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        offsets[E] = (int32_t)R;                 // equals the count total when every index is valid
+        if (shared) offsets[E + 1] = (int32_t)(R + T);
+    }
+    // rows of dropped entries close the last routed group and read token 0 (as in offsets_kernel)
+    for (int64_t r = (int64_t)carry_s + tid; r < R; r += 1024) perm_src[r] = 0;
+}
+
+// ebits: bits that tell apart the keys 0 .. E (E stands for every entry outside [0, E)).
+__global__ __launch_bounds__(256) void chunk_scatter_kernel(const int32_t* __restrict__ idx, int64_t N, int k, int E,
+                                                            int ebits, int64_t chunk, int64_t C,
+                                                            const int32_t* __restrict__ first_row, int64_t R,
+                                                            int32_t* __restrict__ perm_src,
+                                                            int32_t* __restrict__ inv_perm) {
+    __shared__ int32_t next_s[kHistWaves * kHistMaxE];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t c = (int64_t)blockIdx.x * kHistWaves + w;
+    int32_t* next = next_s + w * E;               // next free row of each expert in this chunk
+    if (c < C)
+        for (int e = lane; e < E; e += 64) next[e] = first_row[c * E + e];
+    __syncthreads();
+    if (c >= C) return;
+    const int64_t lo = c * chunk, hi = min(N, lo + chunk);
+    const uint64_t below = (1ull << lane) - 1;    // lanes before this one
+    for (int64_t i0 = lo; i0 < hi; i0 += 64) {    // uniform trip count: every lane takes part in the ballots
+        const int64_t i = i0 + lane;
+        const bool in = i < hi;
+        const int v = in ? idx[i] : -1;
+        const bool ok = v >= 0 && v < E;
+        const int key = ok ? v : E;
+        uint64_t same = ~0ull;                    // lanes whose key equals this lane's
+        for (int b = 0; b < ebits; ++b) {
+            const bool bit = (key >> b) & 1;
+            const uint64_t bal = __ballot(bit);
+            same &= bit ? bal : ~bal;
+        }
+        if (ok) {
+            // one LDS read per lane, then the group's last lane moves the counter past the group (the
+            // wave's LDS operations complete in order, so every read sees the value before the write)
+            const int pos = next[v] + __popcll(same & below);
+            if (pos < R) {
+                perm_src[pos] = (int32_t)(i / k);
+                inv_perm[i] = pos;
+            }
+            if ((same >> lane) == 1ull) next[v] = pos + 1;
+        } else if (in) {
+            inv_perm[i] = -1;                     // out-of-range expert index: dropped
+        }
+    }
+}
+
 // Row gather.  One workgroup (256 threads) per x_perm row, 16-byte vectors.
 __global__ __launch_bounds__(256) void gather_copy_kernel(const uint8_t* __restrict__ x, int64_t T, int64_t R,
                                                           int64_t row_bytes, int32_t* __restrict__ perm_src,
@@ -252,13 +411,27 @@ extern "C" int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, in
     if (ws_bytes < need) return fail(DWDP_ERR_WORKSPACE, "dwdp_permute: workspace too small");
     hipStream_t st = as_stream(stream);
     const int64_t N = T * k, R = N, rows = R + shared * T;
-    const int64_t seg = ((N + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
-    int32_t* wave_counts = static_cast<int32_t*>(ws);
-    int32_t* wave_base = wave_counts + (size_t)E * kWaves;
-    hipLaunchKernelGGL(count_kernel, dim3(E), dim3(1024), 0, st, topk_idx, N, seg, wave_counts);
-    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, wave_counts, E, shared, T, R, offsets, wave_base,
-                       perm_src);
-    hipLaunchKernelGGL(scatter_kernel, dim3(E), dim3(1024), 0, st, topk_idx, N, k, E, seg, wave_base, perm_src, inv_perm);
+    if (E <= kHistMaxE) {
+        const int64_t chunk = hist_chunk(N), C = hist_chunks(N);
+        int ebits = 0;
+        while ((E >> ebits) != 0) ++ebits;        // E itself needs ebits bits
+        int32_t* hist = static_cast<int32_t*>(ws);
+        const dim3 grid((unsigned)((C + kHistWaves - 1) / kHistWaves));
+        hipLaunchKernelGGL(chunk_count_kernel, grid, dim3(64 * kHistWaves), 0, st, topk_idx, N, E, chunk, C, hist);
+        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, st, hist, C, E, shared, T, R, offsets,
+                           perm_src);
+        hipLaunchKernelGGL(chunk_scatter_kernel, grid, dim3(64 * kHistWaves), 0, st, topk_idx, N, k, E, ebits, chunk, C,
+                           hist, R, perm_src, inv_perm);
+    } else {
+        const int64_t seg = ((N + kWaves - 1) / kWaves + kStep - 1) / kStep * kStep;
+        int32_t* wave_counts = static_cast<int32_t*>(ws);
+        int32_t* wave_base = wave_counts + (size_t)E * kWaves;
+        hipLaunchKernelGGL(count_kernel, dim3(E), dim3(1024), 0, st, topk_idx, N, seg, wave_counts);
+        hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, wave_counts, E, shared, T, R, offsets,
+                           wave_base, perm_src);
+        hipLaunchKernelGGL(scatter_kernel, dim3(E), dim3(1024), 0, st, topk_idx, N, k, E, seg, wave_base, perm_src,
+                           inv_perm);
+    }
     if (!gather) {
         if (shared) hipLaunchKernelGGL(shared_rows_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, perm_src, R, T);
     } else if (act_dtype == DWDP_FP8_E4M3) {

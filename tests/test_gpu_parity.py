@@ -126,7 +126,11 @@ def run_permute(idx_np, E, shared, x_t, act_dtype):
     return xp, xs, off.cpu().numpy(), ps.cpu().numpy(), ip.cpu().numpy()
 
 
-PERM_CASES = [(64, 8, 2, 0), (1, 1, 1, 1), (1000, 256, 8, 1), (333, 17, 3, 1), (4097, 64, 4, 0), (2, 8, 8, 1)]
+# Up to 4096 experts the permutation sorts by chunk histograms (chunks of 1024 entries, or more so that
+# there are at most 1024 chunks: 140000 x 8 entries take 973 chunks of 1152, the last one partial); above
+# that, by one workgroup per expert (5000).
+PERM_CASES = [(64, 8, 2, 0), (1, 1, 1, 1), (1000, 256, 8, 1), (333, 17, 3, 1), (4097, 64, 4, 0), (2, 8, 8, 1),
+              (2000, 4096, 8, 0), (300, 5000, 4, 1), (140000, 256, 8, 1)]
 
 
 @pytest.mark.parametrize("T,E,k,shared", PERM_CASES)
@@ -604,12 +608,13 @@ def test_empty_batch_is_a_no_op_for_every_step():
 
 # --------------------------------------------------------------------------------------- dropped entries
 
-def test_permute_and_combine_drop_out_of_range_indices():
+@pytest.mark.parametrize("E", [16, 5000])
+def test_permute_and_combine_drop_out_of_range_indices(E):
     """topk_idx entries outside [0, E) are dropped (include/dwdp.h, dwdp_permute): counted in no expert,
     inv_perm -1, skipped by the combine; offsets[E] stays T*k and the rows closing the last routed group
-    read token 0 (defined, never read back)."""
+    read token 0 (defined, never read back).  E = 16 sorts by chunk histograms, E = 5000 by expert."""
     from split_weight_expert_amd import api
-    T, k, E, H, S = 300, 4, 16, 256, 1
+    T, k, H, S = 300, 4, 256, 1
     rng = np.random.default_rng(17)
     idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
     bad = [(0, 1, -1), (5, 0, E), (17, 3, E + 5), (120, 2, -7), (299, 0, 1 << 20)]
