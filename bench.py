@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--copy-engine", default="kernel", choices=["kernel", "hipmemcpy", "sdma"],
                     help="engine of the pipeline and smi measurements")
     ap.add_argument("--chunk-mib", type=float, default=0, help="prefetch slice size in MiB (default: the workload's 4)")
+    ap.add_argument("--burst-at", default="",
+                    help="paced prefetch: comma-separated stage boundaries (0 block start, 1 after route, 2 after "
+                         "permute, 3 after GEMM1, 4 after GEMM2) at which equal parts of the slice plan are released")
     ap.add_argument("--copy-streams", type=int, default=1,
                     help="deal the prefetch's source regions round-robin over this many copy streams (the kernel "
                          "engine splits --copy-workgroups between them)")
@@ -612,12 +615,29 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block, engine_name):
 
     chunk = int(args.chunk_mib * (1 << 20)) if args.chunk_mib else cfg.chunk_bytes
 
-    def copy(wait=None, done=None):
+    # Paced release (--burst-at): the plan's rounds are cut into equal parts, part j released when the
+    # block passes stage boundary bursts[j] (an event on the compute stream); each part is the same
+    # round-robin plan restricted to its rounds, so together they copy the same slices in the same order.
+    bursts = [int(v) for v in args.burst_at.split(",") if v != ""]
+    assert all(0 <= v <= 4 for v in bursts), "--burst-at takes stage boundaries 0..4"
+    rounds = max(-(-s[2] // chunk) for s in layer.sources)
+    parts = []
+    for j in range(len(bursts)):
+        r0, r1 = rounds * j // len(bursts), rounds * (j + 1) // len(bursts)
+        part = []
+        for src, off, n in layer.sources:
+            a, e = min(n, r0 * chunk), min(n, r1 * chunk)
+            if e > a:
+                part.append((src + a, off + a, e - a))
+        parts.append(part)
+
+    def copy(wait=None, done=None, sources=None):
         # stream i copies source regions i, i + n, ...; the other streams join cs before `done`
+        sources = layer.sources if sources is None else sources
         for st in extra:
             st.wait_stream(cs)
         for i, st in enumerate([cs] + extra):
-            api.prefetch_chunks(dst, layer.sources[i::n_cs], chunk, engine=engine,
+            api.prefetch_chunks(dst, sources[i::n_cs], chunk, engine=engine,
                                 max_workgroups=max(1, args.copy_workgroups // n_cs), copy_stream=st, wait_event=wait,
                                 done_event=done if n_cs == 1 else None)
         if n_cs > 1:
@@ -645,15 +665,16 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block, engine_name):
         t_copy.append(e0.elapsed_time(e1))
 
     def single(with_copy):
-        start = torch.cuda.Event(enable_timing=True)
-        b_end = torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         c_end = torch.cuda.Event(enable_timing=True)
-        start.record(comp)
-        step()
-        b_end.record(comp)
+        step(ev)
+        start, b_end = ev[0], ev[5]
         # the block is enqueued first: the SDMA engine's host enqueue blocks for a while and must not
         # delay the block's launch
-        if with_copy:
+        if with_copy and bursts:
+            for j, (at, part) in enumerate(zip(bursts, parts)):
+                copy(wait=ev[at], done=c_end if j == len(parts) - 1 else None, sources=part)
+        elif with_copy:
             copy(wait=start, done=c_end)
         torch.cuda.synchronize()
         tb = start.elapsed_time(b_end)
@@ -673,9 +694,11 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block, engine_name):
     c_alone = float(np.median(t_copy))
     alone, beside, cbeside = float(np.median(t_alone)), float(np.median(t_blk)), float(np.median(t_cp))
     n_chunks = len(api.prefetch_plan(layer.sources, chunk))
-    log(f"{cfg.name}: prefetch ({engine_name}) copy {c_alone:.2f} ms alone; block {alone:.3f} -> {beside:.3f} ms "
-        f"beside it ({beside / alone - 1:+.1%}), copy done at {cbeside:.2f} ms")
+    log(f"{cfg.name}: prefetch ({engine_name}{', bursts at ' + args.burst_at if bursts else ''}) copy "
+        f"{c_alone:.2f} ms alone; block {alone:.3f} -> {beside:.3f} ms beside it ({beside / alone - 1:+.1%}), "
+        f"copy done at {cbeside:.2f} ms")
     return dict(engine=engine_name, workgroups=args.copy_workgroups if engine_name == "kernel" else None,
+                bursts_at=bursts or None,
                 streams=n_cs, bytes=nbytes, chunk_bytes=chunk, n_chunks=n_chunks,
                 host_enqueue_us_per_chunk=host_s * 1e6 / max(1, n_chunks),
                 copy_ms=c_alone, copy_gbps=nbytes / c_alone / 1e6,
