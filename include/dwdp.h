@@ -33,6 +33,12 @@
  *   - Device-side index values outside their range are not diagnosed (that would
  *     need a host synchronisation); kernels stay in bounds and the results stay
  *     defined.  A topk_idx entry outside [0, E) is dropped: see dwdp_permute.
+ *   - One kernel launch holds fewer than 2^32 work-items.  Per-row and per-token
+ *     kernels walk any count with a bounded grid.  The tiled GEMMs reject, with
+ *     DWDP_ERR_INVALID_ARG ("too large"), a call whose tile grid would not fit:
+ *     the router above ceil(T/64) * ceil(E/64) ~ 2^24 tiles (about 2^26 tokens at
+ *     E = 1024), the grouped FFN above (rows/BM + n_groups) * max(2I, H)/256 ~ 2^23
+ *     tiles (BM the tile height, 256 at prefill: about 75M rows at H = 7168).
  *
  * Layouts (row-major, C order)
  *   x          [T, H]            tokens, bf16 (f32 for the f32 path)

@@ -1276,10 +1276,12 @@ int router_gemm(const void* x, const void* w, int dtype, const float* bias, int6
     if (dtype == DWDP_BF16) {
         p.NT = (E + kBnRouter - 1) / kBnRouter;
         const int64_t grid = ((T + kBmRouter - 1) / kBmRouter) * p.NT;
+        DWDP_REQUIRE(xcd_grid(grid) * 256 <= kMaxLaunchItems, "T too large for one router launch");
         launch_router<kBmRouter, kBnRouter, 2, 2>(p, grid, st);
     } else {
         p.NT = (E + kBnF32 - 1) / kBnF32;
         const int64_t grid = ((T + kBmF32 - 1) / kBmF32) * p.NT;
+        DWDP_REQUIRE(xcd_grid(grid) * 256 <= kMaxLaunchItems, "T too large for one router launch");
         launch_f32<kRouter>(p, grid, st);
     }
     DWDP_LAUNCHED();
@@ -1357,8 +1359,8 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     p2.NT = w_dtype == DWDP_F32 ? H / kBnF32 : H / kBnDma;
     p2.out = static_cast<uint8_t*>(y_perm);
     p2.out_scale = nullptr;
-    DWDP_REQUIRE(maxm * p1.NT < ((int64_t)1 << 31) && maxm * p2.NT < ((int64_t)1 << 31),
-                 "problem too large for one launch");
+    // every expert-GEMM launch holds at most 512 work-items per workgroup
+    DWDP_REQUIRE(xcd_grid(maxm * std::max(p1.NT, p2.NT)) * 512 <= kMaxLaunchItems, "problem too large for one launch");
 
     const bool g1 = stage != 2, g2 = stage != 1;
     if (w_dtype == DWDP_F32) {

@@ -10,6 +10,11 @@
 namespace dwdp {
 
 constexpr int kMaxCopySources = 64;
+// Kernels with one workgroup per row or token launch at most this many workgroups and walk the rest
+// (a launch holds fewer than 2^32 work-items).
+constexpr int64_t kMaxRowGrid = 1 << 20;
+// Work-items one launch may hold.
+constexpr int64_t kMaxLaunchItems = ((int64_t)1 << 32) - 1;
 constexpr int kBmMin = 32;             // smallest expert-GEMM tile height (sizes the m-tile tables)
 constexpr size_t kMTileBytes = 16;     // one entry of an m-tile table
 constexpr int kPermuteWaves = 16;      // waves per count / scatter workgroup of the permutation (E > kHistMaxE)

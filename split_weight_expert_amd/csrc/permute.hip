@@ -25,6 +25,8 @@
 //   gather   one workgroup per x_perm row: bitwise row copy, or per-row fp8
 //            quantisation (scale = amax/448 over 128 columns, code = E4M3(v/s))
 // Every output is bitwise reproducible: the only atomics add integers in LDS.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -308,23 +310,24 @@ __global__ __launch_bounds__(256) void chunk_scatter_kernel(const int32_t* __res
     }
 }
 
-// Row gather.  One workgroup (256 threads) per x_perm row, 16-byte vectors.
+// Row gather.  One workgroup (256 threads) per x_perm row (a bounded grid walks the rows), 16-byte vectors.
 __global__ __launch_bounds__(256) void gather_copy_kernel(const uint8_t* __restrict__ x, int64_t T, int64_t R,
-                                                          int64_t row_bytes, int32_t* __restrict__ perm_src,
+                                                          int64_t rows, int64_t row_bytes, int32_t* __restrict__ perm_src,
                                                           uint8_t* __restrict__ x_perm) {
-    const int64_t r = blockIdx.x;
-    int64_t src;
-    if (r < R) {
-        src = perm_src[r];
-    } else {
-        src = r - R;
-        if (threadIdx.x == 0) perm_src[r] = (int32_t)src;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        int64_t src;
+        if (r < R) {
+            src = perm_src[r];
+        } else {
+            src = r - R;
+            if (threadIdx.x == 0) perm_src[r] = (int32_t)src;
+        }
+        const bool ok = src >= 0 && src < T;
+        const uint4* in = reinterpret_cast<const uint4*>(x + (ok ? src : 0) * row_bytes);
+        uint4* out = reinterpret_cast<uint4*>(x_perm + r * row_bytes);
+        const int64_t nvec = row_bytes / 16;
+        for (int64_t i = threadIdx.x; i < nvec; i += 256) out[i] = ok ? in[i] : uint4{0, 0, 0, 0};
     }
-    const bool ok = src >= 0 && src < T;
-    const uint4* in = reinterpret_cast<const uint4*>(x + (ok ? src : 0) * row_bytes);
-    uint4* out = reinterpret_cast<uint4*>(x_perm + r * row_bytes);
-    const int64_t nvec = row_bytes / 16;
-    for (int64_t i = threadIdx.x; i < nvec; i += 256) out[i] = ok ? in[i] : uint4{0, 0, 0, 0};
 }
 
 // Shared-expert rows of perm_src (token t at row R + t) when no rows are gathered.
@@ -335,47 +338,48 @@ __global__ __launch_bounds__(256) void shared_rows_kernel(int32_t* __restrict__ 
 
 // fp8 gather: 16 lanes per 128-column group, 8 bf16 values (16 bytes) per lane.  perm_src == NULL
 // quantises x row by row (output row r = token r).
-__global__ __launch_bounds__(256) void gather_fp8_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t R, int H,
-                                                         int32_t* __restrict__ perm_src, uint8_t* __restrict__ q,
-                                                         float* __restrict__ qs) {
-    const int64_t r = blockIdx.x;
-    int64_t src;
-    if (r < R) {
-        src = perm_src[r];
-    } else {
-        src = r - R;
-        if (perm_src != nullptr && threadIdx.x == 0) perm_src[r] = (int32_t)src;
-    }
-    const bool ok = src >= 0 && src < T;
-    const int G = H / kFp8Group;
-    const int sub = threadIdx.x & 15;
-    for (int g = threadIdx.x >> 4; g < G; g += 16) {
-        float v[8];
-        if (ok) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(x + src * H + g * kFp8Group + sub * 8);
-            const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = bf16_to_f32((uint16_t)(wds[i] & 0xffffu));
-                v[2 * i + 1] = bf16_to_f32((uint16_t)(wds[i] >> 16));
-            }
+__global__ __launch_bounds__(256) void gather_fp8_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t R,
+                                                         int64_t rows, int H, int32_t* __restrict__ perm_src,
+                                                         uint8_t* __restrict__ q, float* __restrict__ qs) {
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        int64_t src;
+        if (r < R) {
+            src = perm_src[r];
         } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+            src = r - R;
+            if (perm_src != nullptr && threadIdx.x == 0) perm_src[r] = (int32_t)src;
         }
-        float m = 0.0f;
+        const bool ok = src >= 0 && src < T;
+        const int G = H / kFp8Group;
+        const int sub = threadIdx.x & 15;
+        for (int g = threadIdx.x >> 4; g < G; g += 16) {
+            float v[8];
+            if (ok) {
+                const uint4 raw = *reinterpret_cast<const uint4*>(x + src * H + g * kFp8Group + sub * 8);
+                const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = bf16_to_f32((uint16_t)(wds[i] & 0xffffu));
+                    v[2 * i + 1] = bf16_to_f32((uint16_t)(wds[i] >> 16));
+                }
+            } else {
 #pragma unroll
-        for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
-        const float s = m == 0.0f ? 1.0f : m / 448.0f;
-        uint32_t lo = 0, hi = 0;
+                for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+            }
+            float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lo |= (uint32_t)f32_to_e4m3(v[i] / s) << (8 * i);
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hi |= (uint32_t)f32_to_e4m3(v[4 + i] / s) << (8 * i);
-        *reinterpret_cast<uint2*>(q + r * H + g * kFp8Group + sub * 8) = uint2{lo, hi};
-        if (sub == 0) qs[r * G + g] = s;
+            for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
+            const float s = m == 0.0f ? 1.0f : m / 448.0f;
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lo |= (uint32_t)f32_to_e4m3(v[i] / s) << (8 * i);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hi |= (uint32_t)f32_to_e4m3(v[4 + i] / s) << (8 * i);
+            *reinterpret_cast<uint2*>(q + r * H + g * kFp8Group + sub * 8) = uint2{lo, hi};
+            if (sub == 0) qs[r * G + g] = s;
+        }
     }
 }
 
@@ -411,6 +415,7 @@ extern "C" int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, in
     if (ws_bytes < need) return fail(DWDP_ERR_WORKSPACE, "dwdp_permute: workspace too small");
     hipStream_t st = as_stream(stream);
     const int64_t N = T * k, R = N, rows = R + shared * T;
+    const unsigned row_grid = (unsigned)std::min<int64_t>(rows, kMaxRowGrid);
     if (E <= kHistMaxE) {
         const int64_t chunk = hist_chunk(N), C = hist_chunks(N);
         int ebits = 0;
@@ -435,12 +440,11 @@ extern "C" int dwdp_permute(const int32_t* topk_idx, int64_t T, int k, int E, in
     if (!gather) {
         if (shared) hipLaunchKernelGGL(shared_rows_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, perm_src, R, T);
     } else if (act_dtype == DWDP_FP8_E4M3) {
-        hipLaunchKernelGGL(gather_fp8_kernel, dim3((unsigned)rows), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(x), T, R, H, perm_src, static_cast<uint8_t*>(x_perm),
-                           x_perm_scale);
+        hipLaunchKernelGGL(gather_fp8_kernel, dim3(row_grid), dim3(256), 0, st, static_cast<const uint16_t*>(x), T, R,
+                           rows, H, perm_src, static_cast<uint8_t*>(x_perm), x_perm_scale);
     } else {
-        hipLaunchKernelGGL(gather_copy_kernel, dim3((unsigned)rows), dim3(256), 0, st, static_cast<const uint8_t*>(x), T,
-                           R, (int64_t)H * (int64_t)elem_bytes(x_dtype), perm_src, static_cast<uint8_t*>(x_perm));
+        hipLaunchKernelGGL(gather_copy_kernel, dim3(row_grid), dim3(256), 0, st, static_cast<const uint8_t*>(x), T, R,
+                           rows, (int64_t)H * (int64_t)elem_bytes(x_dtype), perm_src, static_cast<uint8_t*>(x_perm));
     }
     DWDP_LAUNCHED();
     return DWDP_OK;
@@ -453,9 +457,9 @@ extern "C" int dwdp_quantize_tokens_fp8(const void* x, int64_t T, int H, void* q
     if (T == 0) return DWDP_OK;
     DWDP_REQUIRE(x && q && q_scale, "null pointer argument");
     DWDP_REQUIRE(aligned16(x) && aligned16(q), "x and q must be 16-byte aligned");
-    hipLaunchKernelGGL(gather_fp8_kernel, dim3((unsigned)T), dim3(256), 0, as_stream(stream),
-                       static_cast<const uint16_t*>(x), T, (int64_t)0, H, static_cast<int32_t*>(nullptr),
-                       static_cast<uint8_t*>(q), q_scale);
+    hipLaunchKernelGGL(gather_fp8_kernel, dim3((unsigned)std::min<int64_t>(T, kMaxRowGrid)), dim3(256), 0,
+                       as_stream(stream), static_cast<const uint16_t*>(x), T, (int64_t)0, T, H,
+                       static_cast<int32_t*>(nullptr), static_cast<uint8_t*>(q), q_scale);
     DWDP_LAUNCHED();
     return DWDP_OK;
 }

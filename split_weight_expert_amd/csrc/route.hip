@@ -12,6 +12,8 @@
 // k rounds of (lane-local best, then a 64-lane butterfly max on (value desc,
 // index asc)) pick the experts in slot order.  Equal logits go to the lower
 // expert index, which makes the selection unique and bitwise reproducible.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -90,56 +92,56 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
                                                    int32_t* __restrict__ idx, float* __restrict__ w) {
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float* row = logits + t * E;
-    float v[kPerLane];
-    bool live[kPerLane];
-#pragma unroll
-    for (int s = 0; s < kPerLane; ++s) {
-        const int e = lane + 64 * s;
-        live[s] = e < E;
-        v[s] = live[s] ? row[e] : 0.0f;
-    }
-    // round j picks slot j; lane j keeps it
-    float my_v = 0.0f, top_v = 0.0f;
-    int my_i = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int bi = 0x7fffffff;
+    for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += (int64_t)gridDim.x * 4) {
+        const float* row = logits + t * E;
+        float v[kPerLane];
+        bool live[kPerLane];
 #pragma unroll
         for (int s = 0; s < kPerLane; ++s) {
             const int e = lane + 64 * s;
-            if (live[s] && (bi == 0x7fffffff || better(v[s], e, bv, bi))) {
-                bv = v[s];
-                bi = e;
-            }
+            live[s] = e < E;
+            v[s] = live[s] ? row[e] : 0.0f;
         }
+        // round j picks slot j; lane j keeps it
+        float my_v = 0.0f, top_v = 0.0f;
+        int my_i = 0;
+        for (int j = 0; j < k; ++j) {
+            float bv = 0.0f;
+            int bi = 0x7fffffff;
 #pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-            const float ov = __shfl_xor(bv, d);
-            const int oi = __shfl_xor(bi, d);
-            if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
-                bv = ov;
-                bi = oi;
+            for (int s = 0; s < kPerLane; ++s) {
+                const int e = lane + 64 * s;
+                if (live[s] && (bi == 0x7fffffff || better(v[s], e, bv, bi))) {
+                    bv = v[s];
+                    bi = e;
+                }
             }
-        }
-        if (j == 0) top_v = bv;
-        if (lane == j) {
-            my_v = bv;
-            my_i = bi;
-        }
 #pragma unroll
-        for (int s = 0; s < kPerLane; ++s)
-            if (lane + 64 * s == bi) live[s] = false;
-    }
-    // weights: softmax over the chosen k, shifted by the largest; summed in slot order
-    const float ex = lane < k ? expf(my_v - top_v) : 0.0f;
-    float sum = 0.0f;
-    for (int j = 0; j < k; ++j) sum += __shfl(ex, j);
-    if (lane < k) {
-        idx[t * k + lane] = my_i;
-        w[t * k + lane] = ex / sum;
+            for (int d = 32; d >= 1; d >>= 1) {
+                const float ov = __shfl_xor(bv, d);
+                const int oi = __shfl_xor(bi, d);
+                if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if (j == 0) top_v = bv;
+            if (lane == j) {
+                my_v = bv;
+                my_i = bi;
+            }
+#pragma unroll
+            for (int s = 0; s < kPerLane; ++s)
+                if (lane + 64 * s == bi) live[s] = false;
+        }
+        // weights: softmax over the chosen k, shifted by the largest; summed in slot order
+        const float ex = lane < k ? expf(my_v - top_v) : 0.0f;
+        float sum = 0.0f;
+        for (int j = 0; j < k; ++j) sum += __shfl(ex, j);
+        if (lane < k) {
+            idx[t * k + lane] = my_i;
+            w[t * k + lane] = ex / sum;
+        }
     }
 }
 
@@ -171,8 +173,8 @@ extern "C" int dwdp_route_topk(const void* x, const void* w_router, int in_dtype
         int rc = router_gemm(x, w_router, in_dtype, bias, T, H, E, logits_out, st);
         if (rc != DWDP_OK) return rc;
     }
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, logits_out, T, E, k, topk_idx,
-                       topk_w);
+    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)std::min<int64_t>((T + 3) / 4, kMaxRowGrid)), dim3(256), 0, st,
+                       logits_out, T, E, k, topk_idx, topk_w);
     DWDP_LAUNCHED();
     return DWDP_OK;
 }

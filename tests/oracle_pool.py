@@ -1,4 +1,5 @@
-"""The oracle's per-expert FFN evaluated in worker processes (test infrastructure only).
+"""The oracle evaluated in worker processes (test infrastructure only): the per-expert FFN, and the
+E4M3 codec over ranges of fp32 bit patterns.
 
 A full-size layer's oracle output for a few hundred tokens needs most of the 256 experts' weights:
 generating them, and for fp8 block-quantising them, takes seconds per expert on one core.  This
@@ -95,3 +96,38 @@ def layer_outputs(cfg, x, idx, w, tokens, layer: int = 0):
         sh = res[cfg.E][pos[cfg.E][t]] if cfg.shared else None
         y[i] = moe.combine(rows, w[t], sh, cfg.dtype)
     return y
+
+
+def _e4m3_task(args):
+    lo, hi, sign = args
+    from oracle import codecs
+    bits = np.arange(lo, hi, dtype=np.uint32) | np.uint32(sign)
+    return codecs.e4m3_encode(bits.view(np.float32))
+
+
+def e4m3_codes(lo: int, hi: int, sign: int, ex, parts: int = 16, timeout: float = 300.0) -> np.ndarray:
+    """The oracle's E4M3 codes of the fp32 bit patterns lo .. hi-1 (each OR-ed with sign), computed in
+    `parts` tasks on the executor ex (a pool from e4m3_pool())."""
+    cuts = [lo + (hi - lo) * i // parts for i in range(parts + 1)]
+    tasks = [(a, b, sign) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    return np.concatenate(list(ex.map(_e4m3_task, tasks, timeout=timeout)))
+
+
+def _bf16_task(args):
+    lo, hi = args
+    from oracle import codecs
+    v = np.arange(lo, hi, dtype=np.uint64).astype(np.uint32).view(np.float32).astype(np.float64)
+    return codecs.bf16_bits(0.0 + v)          # a sum that starts at +0, as the combine's does
+
+
+def bf16_codes(lo: int, hi: int, ex, parts: int = 16, timeout: float = 300.0) -> np.ndarray:
+    """bf16 storage bits of the oracle's rounding of 0 + x for the fp32 bit patterns x = lo .. hi-1."""
+    cuts = [lo + (hi - lo) * i // parts for i in range(parts + 1)]
+    tasks = [(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    return np.concatenate(list(ex.map(_bf16_task, tasks, timeout=timeout)))
+
+
+def e4m3_pool():
+    """A pool of spawned CPU workers for e4m3_codes and bf16_codes (use as a context manager)."""
+    return cf.ProcessPoolExecutor(max_workers=pool_size(), mp_context=mp.get_context("spawn"),
+                                  initializer=_init_worker)

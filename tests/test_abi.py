@@ -198,3 +198,17 @@ def test_store_rejects_placements_outside_its_buffers():
         with pytest.raises(ValueError):
             st.table(good + bad, "cpu")
     del torch
+
+
+def test_launch_sizes_beyond_one_dispatch_are_rejected(lib):
+    """A dispatch holds fewer than 2^32 work-items.  The per-row and per-token kernels walk any count with a
+    bounded grid; the tiled GEMMs reject a problem whose tile grid would not fit, before anything is
+    launched (the pointers here are never dereferenced)."""
+    E_ = lib_mod.DWDP_ERR_INVALID_ARG
+    # router: 2^30 tokens of 1024 experts is 2^28 tiles of 64 x 64
+    expect(E_, lib.dwdp_route_topk(FAKE, FAKE, 1, None, 1 << 30, 64, 1024, 8, FAKE, FAKE, FAKE, None), lib,
+           "too large")
+    # grouped FFN: 2^31 - 1 rows in one group is 2^23 tiles of 256 rows, times 512 work-items
+    rows = (1 << 31) - 1
+    expect(E_, lib.dwdp_moe_grouped_ffn(FAKE, 1, FAKE, FAKE, None, rows, 256, 128, 1, FAKE, FAKE, 1 << 62, None), lib,
+           "too large")

@@ -5,6 +5,8 @@ bit-exact for routing indices, permutation and copies, and the stated
 tolerances for floating-point outputs (fp32 1e-5 max relative; bf16 2e-2
 max / 2e-3 mean; fp8 6e-2 max).
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -202,6 +204,77 @@ def test_e4m3_device_encoder_on_every_bf16_pattern():
     xq, xs, *_ = run_permute(idx, 1, 0, x, api.FP8_E4M3)
     assert np.all(xs.cpu().numpy() == 1.0)
     np.testing.assert_array_equal(xq.cpu().numpy(), codecs.e4m3_encode(rows))
+
+
+def test_e4m3_device_encoder_on_every_fp32_pattern_up_to_448():
+    """The device's fp32 -> E4M3 encoder on every fp32 value of magnitude <= 448 (normals, subnormals and
+    both zeros, both signs: 2 x 1,138,753,537 bit patterns) against the oracle codec.  The values go
+    through the block quantiser with unit scales: element 0 of every 128 x 128 block holds 448, so the
+    block's scale is 448 / 448 = 1 and every code is the encoder's code of the value itself."""
+    from split_weight_expert_amd import api
+    from tests import oracle_pool
+    top = 0x43E00000                                   # bit pattern of 448.0
+    NB, PER = 8192, 128 * 128 - 1                      # blocks per launch, patterns per block
+    chunk = NB * PER
+    w = torch.empty(NB * 128, 128, dtype=torch.float32, device=DEV)
+    q = torch.empty(NB * 128, 128, dtype=torch.uint8, device=DEV)
+    s = torch.empty(NB, 1, dtype=torch.float32, device=DEV)
+    wv, qv = w.view(NB, 128 * 128), q.view(NB, 128 * 128)
+    checked = 0
+    t0 = time.time()
+    with oracle_pool.e4m3_pool() as ex:
+        for sign in (0, 0x80000000):
+            for lo in range(0, top + 1, chunk):
+                hi = min(top + 1, lo + chunk)
+                bits = torch.arange(lo, lo + chunk, dtype=torch.int64, device=DEV)
+                bits = torch.where(bits < hi, bits, torch.zeros_like(bits)) | sign      # padding: +-0
+                bits = torch.where(bits >= 2 ** 31, bits - 2 ** 32, bits).to(torch.int32)
+                wv[:, 0] = 448.0
+                wv[:, 1:] = bits.view(torch.float32).view(NB, PER)
+                api.quantize_weight_fp8(w, q, s)
+                torch.cuda.synchronize()
+                assert bool((s == 1.0).all()) and bool((qv[:, 0] == 0x7E).all())
+                got = qv[:, 1:].reshape(-1)[:hi - lo].cpu().numpy()
+                ref = oracle_pool.e4m3_codes(lo, hi, sign, ex)
+                bad = np.flatnonzero(got != ref)
+                assert bad.size == 0, (f"{bad.size} codes differ, first at bit pattern "
+                                       f"{(lo + int(bad[0])) | sign:#010x}: device {got[bad[0]]:#04x}, "
+                                       f"oracle {ref[bad[0]]:#04x}")
+                checked += hi - lo
+                print(f"[e4m3] sign {sign >> 31}: patterns {lo:#010x}..{hi - 1:#010x} equal "
+                      f"({checked} so far, {time.time() - t0:.0f} s)", flush=True)
+    assert checked == 2 * (top + 1)
+
+
+def test_bf16_device_rounding_on_every_fp32_pattern():
+    """The device's fp32 -> bf16 rounding on all 2^32 fp32 bit patterns against the oracle's.  The values
+    go through the combine with k = 1, no shared expert, y_perm rows of ones and gate weight w[t] = the
+    pattern, so y[t] is the rounding of 0 + w[t] * 1 (the combine's sum starts at +0: -0 gives +0).  The
+    oracle's rounding keeps no NaN payload, so a NaN input only has to give a NaN."""
+    from split_weight_expert_amd import api
+    from tests import oracle_pool
+    T, H = 1 << 26, 8
+    yp = torch.ones(T, H, dtype=torch.bfloat16, device=DEV)
+    inv = torch.arange(T, dtype=torch.int32, device=DEV).view(T, 1)
+    w = torch.empty(T, 1, dtype=torch.float32, device=DEV)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    t0 = time.time()
+    with oracle_pool.e4m3_pool() as ex:
+        for lo in range(0, 1 << 32, T):
+            bits = torch.arange(lo, lo + T, dtype=torch.int64, device=DEV)
+            bits = torch.where(bits >= 2 ** 31, bits - 2 ** 32, bits).to(torch.int32)
+            w.view(-1).copy_(bits.view(torch.float32))
+            api.combine(yp, inv, w, 0, y)
+            got = y[:, 0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            ref = oracle_pool.bf16_codes(lo, lo + T, ex)
+            pat = np.arange(lo, lo + T, dtype=np.uint64).astype(np.uint32)
+            nan = (pat & 0x7FFFFFFF) > 0x7F800000
+            bad = np.flatnonzero((got != ref) & ~nan)
+            assert bad.size == 0, (f"{bad.size} results differ, first at bit pattern {int(pat[bad[0]]):#010x}: "
+                                   f"device {got[bad[0]]:#06x}, oracle {ref[bad[0]]:#06x}")
+            assert np.all((got[nan] & 0x7FFF) > 0x7F80), "a NaN input gave a non-NaN"
+            if (lo // T) % 8 == 7:
+                print(f"[bf16] patterns up to {lo + T - 1:#010x} equal ({time.time() - t0:.0f} s)", flush=True)
 
 
 # --------------------------------------------------------------------------------------- weights fp8
@@ -512,6 +585,47 @@ def test_token_quantiser_is_bit_exact():
     qr, sr = omoe.quantize_groups(xt.float().cpu().numpy())
     np.testing.assert_array_equal(q.cpu().numpy(), qr)
     np.testing.assert_array_equal(s.cpu().numpy(), sr)
+
+
+def test_per_token_kernels_walk_more_tokens_than_their_grid():
+    """The per-token kernels launch at most 2^20 workgroups and walk the rest: token quantiser and combine
+    (one workgroup per token) at 2^20 + 37 tokens, top-k (four tokens per workgroup) at 2^22 + 11."""
+    from split_weight_expert_amd import api
+    rng = np.random.default_rng(41)
+    T, H = (1 << 20) + 37, 128
+    x = torch.from_numpy(rng.normal(size=(T, H)).astype(np.float32)).to(DEV, torch.bfloat16)
+    q = torch.empty(T, H, dtype=torch.uint8, device=DEV)
+    s = torch.empty(T, 1, dtype=torch.float32, device=DEV)
+    api.quantize_tokens_fp8(x, q, s)
+    torch.cuda.synchronize()
+    qr, sr = omoe.quantize_groups(x.float().cpu().numpy())
+    np.testing.assert_array_equal(q.cpu().numpy(), qr)
+    np.testing.assert_array_equal(s.cpu().numpy(), sr)
+    # combine, k = 2 with a shared row, H = 8
+    k, Hc = 2, 8
+    yp = torch.from_numpy(rng.normal(size=(T * k + T, Hc)).astype(np.float32)).to(DEV, torch.bfloat16)
+    ip_np = rng.permutation(T * k).astype(np.int32).reshape(T, k)
+    w_np = rng.random((T, k)).astype(np.float32)
+    y = torch.empty(T, Hc, dtype=torch.bfloat16, device=DEV)
+    api.combine(yp, torch.from_numpy(ip_np).to(DEV), torch.from_numpy(w_np).to(DEV), 1, y)
+    torch.cuda.synchronize()
+    ypn = to_np(yp)
+    acc = np.zeros((T, Hc))
+    for j in range(k):                           # the oracle's combine, vectorised over tokens
+        acc = acc + w_np[:, j:j + 1].astype(np.float64) * ypn[ip_np[:, j]]
+    ref = codecs.bf16_round(acc + ypn[T * k:])
+    assert_close(to_np(y), ref, "bf16", "combine over 2^20 + 37 tokens")
+    # top-k on f32 logits of 2^22 + 11 tokens, E = 8, k = 3
+    T2, Hr, E, kk = (1 << 22) + 11, 16, 8, 3
+    xr = torch.from_numpy(rng.normal(size=(T2, Hr)).astype(np.float32)).to(DEV)
+    wr = torch.from_numpy(rng.normal(size=(E, Hr)).astype(np.float32)).to(DEV)
+    logits = torch.empty(T2, E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T2, kk, dtype=torch.int32, device=DEV)
+    wt = torch.empty(T2, kk, dtype=torch.float32, device=DEV)
+    api.route_topk(xr, wr, None, kk, logits, idx, wt)
+    torch.cuda.synchronize()
+    gl = logits.cpu().numpy()
+    np.testing.assert_array_equal(idx.cpu().numpy(), omoe.topk_select(gl, kk))
 
 
 @pytest.mark.parametrize("shared", [0, 1])
