@@ -29,25 +29,28 @@ def _init_worker():
         pass
 
 
-def expert_rows(cfg, e: int, x_rows: np.ndarray, layer: int = 0, parts: bool = False, with_wd: bool = False):
+def expert_rows(cfg, e: int, x_rows: np.ndarray, layer: int = 0, parts: bool = False, with_wd: bool = False,
+                precision: str | None = None):
     """Oracle outputs of expert e (e == E: the shared expert) for the given token rows (float32 [n, H]):
     Y [n, H] float64, or the full expert_ffn_parts dict when parts (with the prepared down weights
-    under "wd" when with_wd)."""
+    under "wd" when with_wd).  precision overrides the workload's policy (e.g. "f32": the unquantised,
+    unrounded fp64 FFN of the same generated weights)."""
     import synth
     from oracle import moe
-    wts = moe.prepare_weights(*synth.expert_weights(cfg, e, layer), cfg.dtype)
-    X = moe.prepare_tokens(x_rows, cfg.dtype)
+    pol = precision or cfg.dtype
+    wts = moe.prepare_weights(*synth.expert_weights(cfg, e, layer), pol)
+    X = moe.prepare_tokens(x_rows, pol)
     if parts:
-        p = moe.expert_ffn_parts(X, *wts, cfg.dtype)
+        p = moe.expert_ffn_parts(X, *wts, pol)
         if with_wd:
             p["wd"] = wts[2]
         return p
-    return moe.expert_ffn(X, *wts, cfg.dtype)
+    return moe.expert_ffn(X, *wts, pol)
 
 
 def _task(args):
-    cfg, e, rows, layer, parts, with_wd = args
-    return e, expert_rows(cfg, e, rows, layer, parts, with_wd)
+    cfg, e, rows, layer, parts, with_wd, precision = args
+    return e, expert_rows(cfg, e, rows, layer, parts, with_wd, precision)
 
 
 def pool_size() -> int:
@@ -58,7 +61,8 @@ def pool_size() -> int:
     return max(1, min(16, n))
 
 
-def map_experts(cfg, jobs, layer: int = 0, parts: bool = False, with_wd=(), timeout: float = 900.0):
+def map_experts(cfg, jobs, layer: int = 0, parts: bool = False, with_wd=(), timeout: float = 900.0,
+                precision: str | None = None):
     """jobs: {expert: token rows float32 [n, H]} -> {expert: oracle result}, evaluated in parallel.
 
     Workers are spawned (they re-import the caller's main module by name, so the caller must be an
@@ -69,7 +73,7 @@ def map_experts(cfg, jobs, layer: int = 0, parts: bool = False, with_wd=(), time
     out = {}
     with cf.ProcessPoolExecutor(max_workers=min(pool_size(), max(1, len(order))), mp_context=ctx,
                                 initializer=_init_worker) as ex:
-        for e, res in ex.map(_task, [(cfg, e, jobs[e], layer, parts, e in with_wd) for e in order],
+        for e, res in ex.map(_task, [(cfg, e, jobs[e], layer, parts, e in with_wd, precision) for e in order],
                              timeout=timeout):
             out[e] = res
     return out

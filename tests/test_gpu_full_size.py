@@ -103,6 +103,17 @@ def sample_tokens(idx, counts, T, n):
     return sorted(out)
 
 
+def _token_jobs(toks, idx, cfg):
+    """expert -> the sampled tokens it computes (their k chosen experts and the shared expert)."""
+    jobs = {}
+    for t in toks:
+        for j in range(cfg.k):
+            jobs.setdefault(int(idx[t, j]), []).append(int(t))
+        if cfg.shared:
+            jobs.setdefault(cfg.E, []).append(int(t))
+    return jobs
+
+
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("name,n_tokens", [
     ("prefill8k_bf16", 512),
@@ -213,3 +224,18 @@ def test_full_size_block(name, n_tokens):
     mx, mn = assert_close(y, ref, cfg.dtype, f"{name} {len(toks)} sampled tokens")
     print(f"[full-size] {name}: {len(toks)} tokens max rel {mx:.2e} mean rel {mn:.2e} ({time.time() - t0:.0f} s)",
           flush=True)
+
+    # ---- the same tokens against unquantised, unrounded math (the oracle's fp64 FFN of the generated
+    # weights and the token values, same routing): the error the precision policy itself costs.  Reported,
+    # with only a coarse bar that catches a broken path.
+    tj = {e: np.array(sorted(set(ts))) for e, ts in _token_jobs(toks, idx, cfg).items()}
+    uq = oracle_pool.map_experts(cfg, {e: x[ts] for e, ts in tj.items()}, precision="f32")
+    upos = {e: {int(t): i for i, t in enumerate(ts)} for e, ts in tj.items()}
+    exact = np.zeros_like(y, dtype=np.float64)
+    for i, t in enumerate(toks):
+        rows = np.stack([uq[int(idx[t, j])][upos[int(idx[t, j])][t]] for j in range(cfg.k)])
+        sh = uq[cfg.E][upos[cfg.E][t]] if cfg.shared else None
+        exact[i] = omoe.combine(rows, gw[t], sh, "f32")
+    emx, emn = rel_err(y, exact)
+    print(f"[full-size] {name}: against unquantised fp64 math: max rel {emx:.2e} mean rel {emn:.2e}", flush=True)
+    assert emn <= (0.1 if cfg.dtype == "fp8" else 1e-2), f"{name}: mean rel {emn:.2e} against unquantised math"
