@@ -45,7 +45,7 @@ struct MTile {
     int32_t g;    // group
     int32_t m0;   // index of the group's first m-tile
     int32_t mc;   // the group's m-tile count
-    int32_t pad;
+    int32_t h;    // rows per m-tile of the group (the last one may hold fewer)
 };
 static_assert(sizeof(MTile) == kMTileBytes, "the workspace layout sizes the m-tile tables");
 
@@ -154,8 +154,8 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
     t.nt = rem / ms;
     const int mi = mfirst + rem % ms;
     const int r0 = p.offsets[m.g], r1 = p.offsets[m.g + 1];
-    t.row0 = (int64_t)r0 + (int64_t)mi * BM;
-    t.nrows = min(BM, r1 - (int)t.row0);
+    t.row0 = (int64_t)r0 + (int64_t)mi * m.h;
+    t.nrows = min(m.h, r1 - (int)t.row0);
     return true;
 }
 
@@ -168,6 +168,9 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
 constexpr int kSortGroups = 4096;
 #ifndef DWDP_SPARSE_ROWS
 #define DWDP_SPARSE_ROWS 0
+#endif
+#ifndef DWDP_BALANCED_MTILES
+#define DWDP_BALANCED_MTILES 0
 #endif
 
 template <int BM>
@@ -252,7 +255,14 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
         const int excl = before + incl - c;
         if (g < G) {
             if (pass == 0) mprefix[g] = excl;
-            for (int m = 0; m < c; ++m) table[excl + m] = MTile{g, excl, c, 0};
+            // m-tile height: BM, or with DWDP_BALANCED_MTILES the group's rows split evenly over its c
+            // m-tiles (in whole 32-row blocks), so that its tiles take about the same time
+            int h = BM;
+            if (DWDP_BALANCED_MTILES && c > 1) {
+                const int n = offsets[g + 1] - offsets[g];
+                h = ((n + c - 1) / c + 31) / 32 * 32;
+            }
+            for (int m = 0; m < c; ++m) table[excl + m] = MTile{g, excl, c, h};
         }
         __syncthreads();
         if (tid == 0) {

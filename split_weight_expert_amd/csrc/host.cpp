@@ -145,6 +145,9 @@ const char* dwdp_version(void) {
 #ifdef DWDP_SPARSE_ROWS
            " sparse-rows=" DWDP_STR(DWDP_SPARSE_ROWS)
 #endif
+#ifdef DWDP_BALANCED_MTILES
+           " balanced-mtiles=" DWDP_STR(DWDP_BALANCED_MTILES)
+#endif
 #ifdef DWDP_WEIGHT_CPOL
            " weight-cpol=" DWDP_STR(DWDP_WEIGHT_CPOL)
 #endif
