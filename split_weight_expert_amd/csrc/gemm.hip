@@ -76,6 +76,7 @@ struct Tile {
     int nt;
     int64_t row0;
     int nrows;
+    int mc;       // m-tiles of the group (1: the tile is the only reader of its weight slab)
 };
 
 // Row of the activation matrix that holds permuted row prow: itself, or its token (clamped).
@@ -123,6 +124,7 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
         t.nt = lin / mt_router;
         t.row0 = (int64_t)mi * BM;
         t.nrows = (int)min((int64_t)BM, p.rows - t.row0);
+        t.mc = 1;
         return true;
     }
     const MTile m = p.mtiles[lin / p.NT];
@@ -156,6 +158,7 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
     const int r0 = p.offsets[m.g], r1 = p.offsets[m.g + 1];
     t.row0 = (int64_t)r0 + (int64_t)mi * m.h;
     t.nrows = min(m.h, r1 - (int)t.row0);
+    t.mc = m.mc;
     return true;
 }
 
@@ -421,6 +424,14 @@ __global__ __launch_bounds__(WM * WN * 64) void router_mfma_kernel(GemmParams p)
 #ifndef DWDP_ACT_CPOL
 #define DWDP_ACT_CPOL 0
 #endif
+// Weight loads of a tile whose group has a single m-tile are the only reads of those lines: they use
+// DWDP_STREAM_WEIGHT_CPOL (default 2, non-temporal), which streams HBM about 13% faster than the default
+// policy with this kernel's loads (7.0 against 6.2 TB/s).  Slabs that several m-tiles share keep
+// DWDP_WEIGHT_CPOL, so that the tiles after the first find them in L2.
+#ifndef DWDP_STREAM_WEIGHT_CPOL
+#define DWDP_STREAM_WEIGHT_CPOL 2
+#endif
+constexpr int kStreamWeightCpol = DWDP_STREAM_WEIGHT_CPOL;
 template <int CPOL = 0>
 __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -519,7 +530,7 @@ __device__ __forceinline__ int aslot(int row, int chunk) {
 // MWV (compile-time: the loop body is straight-line code; only the LDS ring is waited on, and only
 // here, with vmcnt).  Every wave loads its share of the MA blocks' rows whatever its MWV, and a wave
 // with MWV == 0 only loads and keeps the barriers.
-template <int BM, int ROWB, int MA, int MWV, int KIND, bool FP8>
+template <int BM, int ROWB, int MA, int MWV, int KIND, bool FP8, int WPOL>
 __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c, uint8_t* smem,
                                           const float* s_bscale) {
     using C = FragCfg<BM, ROWB, FP8>;
@@ -579,7 +590,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
 #pragma unroll
         for (int i = 0; i < AI; ++i) dma16<DWDP_ACT_CPOL>(ga[i] + (size_t)kt * ROWB, st + (wave * AI + i) * 1024);
 #pragma unroll
-        for (int q = 0; q < BIW; ++q) dma16<DWDP_WEIGHT_CPOL>(gb[q] + (size_t)kt * BF * 1024, st + lb[q]);
+        for (int q = 0; q < BIW; ++q) dma16<WPOL>(gb[q] + (size_t)kt * BF * 1024, st + lb[q]);
         if constexpr (FP8) scale_dma(kt, st);
     };
     // DMA instructions q0 .. q1-1 of a step's PER (activation rows, weight fragments, row scales)
@@ -589,7 +600,7 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         for (int q = 0; q < PER; ++q) {
             if (q < q0 || q >= q1) continue;
             if (q < AI) dma16<DWDP_ACT_CPOL>(ga[q] + (size_t)kt * ROWB, st + (wave * AI + q) * 1024);
-            else if (q < AI + BIW) dma16<DWDP_WEIGHT_CPOL>(gb[q - AI] + (size_t)kt * BF * 1024, st + lb[q - AI]);
+            else if (q < AI + BIW) dma16<WPOL>(gb[q - AI] + (size_t)kt * BF * 1024, st + lb[q - AI]);
             else if constexpr (FP8) scale_dma(kt, st);
         }
     };
@@ -1053,44 +1064,54 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
     }
     // active 32-row m-blocks
     const int ma = (c.t.nrows + 31) / 32;
-    if constexpr (C::NW == 4) {
-        if constexpr (C::MI == 1) {
-            frag_tile<BM, ROWB, 1, 1, KIND, FP8>(p, c, smem, s_bscale);
-        } else if constexpr (C::MI == 2) {
-            if (ma <= 1) frag_tile<BM, ROWB, 1, 1, KIND, FP8>(p, c, smem, s_bscale);
-            else frag_tile<BM, ROWB, 2, 2, KIND, FP8>(p, c, smem, s_bscale);
+    auto dispatch = [&](auto pol) __attribute__((always_inline)) {
+        constexpr int WPOL = decltype(pol)::value;
+        if constexpr (C::NW == 4) {
+            if constexpr (C::MI == 1) {
+                frag_tile<BM, ROWB, 1, 1, KIND, FP8, WPOL>(p, c, smem, s_bscale);
+            } else if constexpr (C::MI == 2) {
+                if (ma <= 1) frag_tile<BM, ROWB, 1, 1, KIND, FP8, WPOL>(p, c, smem, s_bscale);
+                else frag_tile<BM, ROWB, 2, 2, KIND, FP8, WPOL>(p, c, smem, s_bscale);
+            } else {
+                static_assert(C::MI == 4, "4-wave tiles hold at most 128 rows");
+                if (ma <= 1) frag_tile<BM, ROWB, 1, 1, KIND, FP8, WPOL>(p, c, smem, s_bscale);
+                else if (ma == 2) frag_tile<BM, ROWB, 2, 2, KIND, FP8, WPOL>(p, c, smem, s_bscale);
+                else if (ma == 3) frag_tile<BM, ROWB, 3, 3, KIND, FP8, WPOL>(p, c, smem, s_bscale);
+                else frag_tile<BM, ROWB, 4, 4, KIND, FP8, WPOL>(p, c, smem, s_bscale);
+            }
         } else {
-            static_assert(C::MI == 4, "4-wave tiles hold at most 128 rows");
-            if (ma <= 1) frag_tile<BM, ROWB, 1, 1, KIND, FP8>(p, c, smem, s_bscale);
-            else if (ma == 2) frag_tile<BM, ROWB, 2, 2, KIND, FP8>(p, c, smem, s_bscale);
-            else if (ma == 3) frag_tile<BM, ROWB, 3, 3, KIND, FP8>(p, c, smem, s_bscale);
-            else frag_tile<BM, ROWB, 4, 4, KIND, FP8>(p, c, smem, s_bscale);
+            // two row parts of MIW m-blocks: the first part takes the first active blocks; a part without
+            // active rows runs the load-only variant (the same loads as the active part's)
+            constexpr int MIW = C::MIW;
+            const int rh = wave >> 2;
+            auto run = [&](auto tag) {
+                constexpr int MA = decltype(tag)::value;
+                constexpr int W0 = MA < MIW ? MA : MIW, W1 = MA > MIW ? MA - MIW : 0;
+                if (rh == 0) frag_tile<BM, ROWB, MA, W0, KIND, FP8, WPOL>(p, c, smem, s_bscale);
+                else if constexpr (W1 > 0) frag_tile<BM, ROWB, MA, W1, KIND, FP8, WPOL>(p, c, smem, s_bscale);
+                else frag_tile<BM, ROWB, MIW, 0, KIND, FP8, WPOL>(p, c, smem, s_bscale);
+            };
+            if constexpr (MIW == 4) {
+                if (ma <= 1) run(std::integral_constant<int, 1>{});
+                else if (ma == 2) run(std::integral_constant<int, 2>{});
+                else if (ma <= 4) run(std::integral_constant<int, 4>{});
+                else if (ma <= 6) run(std::integral_constant<int, 6>{});
+                else run(std::integral_constant<int, 8>{});
+            } else {
+                static_assert(MIW == 2, "8-wave tiles are 128 (fp8) or 256 (bf16) rows");
+                if (ma <= 1) run(std::integral_constant<int, 1>{});
+                else if (ma == 2) run(std::integral_constant<int, 2>{});
+                else if (ma == 3) run(std::integral_constant<int, 3>{});
+                else run(std::integral_constant<int, 4>{});
+            }
         }
+    };
+    // A group with one m-tile reads each weight slab exactly once: stream it (kStreamWeightCpol)
+    if constexpr (kStreamWeightCpol == DWDP_WEIGHT_CPOL) {
+        dispatch(std::integral_constant<int, DWDP_WEIGHT_CPOL>{});
     } else {
-        // two row parts of MIW m-blocks: the first part takes the first active blocks; a part without
-        // active rows runs the load-only variant (the same loads as the active part's)
-        constexpr int MIW = C::MIW;
-        const int rh = wave >> 2;
-        auto run = [&](auto tag) {
-            constexpr int MA = decltype(tag)::value;
-            constexpr int W0 = MA < MIW ? MA : MIW, W1 = MA > MIW ? MA - MIW : 0;
-            if (rh == 0) frag_tile<BM, ROWB, MA, W0, KIND, FP8>(p, c, smem, s_bscale);
-            else if constexpr (W1 > 0) frag_tile<BM, ROWB, MA, W1, KIND, FP8>(p, c, smem, s_bscale);
-            else frag_tile<BM, ROWB, MIW, 0, KIND, FP8>(p, c, smem, s_bscale);
-        };
-        if constexpr (MIW == 4) {
-            if (ma <= 1) run(std::integral_constant<int, 1>{});
-            else if (ma == 2) run(std::integral_constant<int, 2>{});
-            else if (ma <= 4) run(std::integral_constant<int, 4>{});
-            else if (ma <= 6) run(std::integral_constant<int, 6>{});
-            else run(std::integral_constant<int, 8>{});
-        } else {
-            static_assert(MIW == 2, "8-wave tiles are 128 (fp8) or 256 (bf16) rows");
-            if (ma <= 1) run(std::integral_constant<int, 1>{});
-            else if (ma == 2) run(std::integral_constant<int, 2>{});
-            else if (ma == 3) run(std::integral_constant<int, 3>{});
-            else run(std::integral_constant<int, 4>{});
-        }
+        if (c.t.mc == 1) dispatch(std::integral_constant<int, kStreamWeightCpol>{});
+        else dispatch(std::integral_constant<int, DWDP_WEIGHT_CPOL>{});
     }
 }
 

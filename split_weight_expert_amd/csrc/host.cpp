@@ -151,6 +151,9 @@ const char* dwdp_version(void) {
 #ifdef DWDP_WEIGHT_CPOL
            " weight-cpol=" DWDP_STR(DWDP_WEIGHT_CPOL)
 #endif
+#ifdef DWDP_STREAM_WEIGHT_CPOL
+           " stream-weight-cpol=" DWDP_STR(DWDP_STREAM_WEIGHT_CPOL)
+#endif
 #ifdef DWDP_ACT_CPOL
            " act-cpol=" DWDP_STR(DWDP_ACT_CPOL)
 #endif
