@@ -13,6 +13,19 @@ namespace dwdp {
 namespace {
 
 constexpr int kMaxK = 64;
+#ifndef DWDP_COMBINE_NT
+#define DWDP_COMBINE_NT 1
+#endif
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load16(const uint4* q) {
+    if constexpr (DWDP_COMBINE_NT) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
+        return uint4{v[0], v[1], v[2], v[3]};
+    }
+    return *q;
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict__ y_perm,
@@ -43,12 +56,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict_
                     const int j = j0 + u;
                     if (j < nsrc) {
                         const int64_t row = j < k ? (s_row[j] >= 0 ? s_row[j] : 0) : shared_row;
+                        // each y_perm element is read once: non-temporal loads (DWDP_COMBINE_NT) stream it
                         if (BF16) {
-                            raw[u] = *reinterpret_cast<const uint4*>(y_perm + (row * H + c * 8) * 2);
+                            const uint4* q = reinterpret_cast<const uint4*>(y_perm + (row * H + c * 8) * 2);
+                            raw[u] = load16(q);
                         } else {
                             const uint4* q = reinterpret_cast<const uint4*>(y_perm + (row * H + c * 8) * 4);
-                            raw[2 * u] = q[0];
-                            raw[2 * u + 1] = q[1];
+                            raw[2 * u] = load16(q);
+                            raw[2 * u + 1] = load16(q + 1);
                         }
                     }
                 }

@@ -428,6 +428,9 @@ __global__ __launch_bounds__(WM * WN * 64) void router_mfma_kernel(GemmParams p)
 // DWDP_STREAM_WEIGHT_CPOL (default 2, non-temporal), which streams HBM about 13% faster than the default
 // policy with this kernel's loads (7.0 against 6.2 TB/s).  Slabs that several m-tiles share keep
 // DWDP_WEIGHT_CPOL, so that the tiles after the first find them in L2.
+#ifndef DWDP_YPERM_NT
+#define DWDP_YPERM_NT 1
+#endif
 #ifndef DWDP_STREAM_WEIGHT_CPOL
 #define DWDP_STREAM_WEIGHT_CPOL 2
 #endif
@@ -1017,9 +1020,13 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
         uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
         for (int q = threadIdx.x; q < BM * 32; q += NW * 64) {
             const int row = q >> 5, c = q & 31;
-            if (row < t.nrows)
-                *reinterpret_cast<u32x4*>(out + (size_t)(t.row0 + row) * p.N + t.nt * 256 + c * 8) =
-                    *reinterpret_cast<const u32x4*>(stg + row * 512 + ((c ^ (row & 31)) << 4));
+            if (row < t.nrows) {
+                u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)(t.row0 + row) * p.N + t.nt * 256 + c * 8);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * 512 + ((c ^ (row & 31)) << 4));
+                // y_perm is read once, by the combine, and is larger than the caches: stream it out
+                if constexpr (DWDP_YPERM_NT) __builtin_nontemporal_store(v, dst);
+                else *dst = v;
+            }
         }
     }
 }

@@ -154,6 +154,12 @@ const char* dwdp_version(void) {
 #ifdef DWDP_STREAM_WEIGHT_CPOL
            " stream-weight-cpol=" DWDP_STR(DWDP_STREAM_WEIGHT_CPOL)
 #endif
+#ifdef DWDP_YPERM_NT
+           " yperm-nt=" DWDP_STR(DWDP_YPERM_NT)
+#endif
+#ifdef DWDP_COMBINE_NT
+           " combine-nt=" DWDP_STR(DWDP_COMBINE_NT)
+#endif
 #ifdef DWDP_ACT_CPOL
            " act-cpol=" DWDP_STR(DWDP_ACT_CPOL)
 #endif
