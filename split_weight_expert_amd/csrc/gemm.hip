@@ -428,6 +428,7 @@ __global__ __launch_bounds__(WM * WN * 64) void router_mfma_kernel(GemmParams p)
 // DWDP_STREAM_WEIGHT_CPOL (default 2, non-temporal), which streams HBM about 13% faster than the default
 // policy with this kernel's loads (7.0 against 6.2 TB/s).  Slabs that several m-tiles share keep
 // DWDP_WEIGHT_CPOL, so that the tiles after the first find them in L2.
+// GEMM2 writes y_perm with non-temporal stores (DWDP_YPERM_NT, default 1): the combine reads it once.
 #ifndef DWDP_YPERM_NT
 #define DWDP_YPERM_NT 1
 #endif
