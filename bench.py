@@ -594,6 +594,23 @@ def measure_pipeline(layer, block, step, args, cfg, pf):
                      "block to the end of the last layer")
 
 
+def burst_parts(sources, chunk, n):
+    """The slice plan's rounds cut into n equal parts: part j is the list of (src, dst_offset, bytes) that,
+    planned on its own, gives the rounds [R*j/n, R*(j+1)/n) of the whole plan (R rounds), in the same
+    order, so the parts together copy the same slices in the same order."""
+    rounds = max(-(-s[2] // chunk) for s in sources)
+    parts = []
+    for j in range(n):
+        r0, r1 = rounds * j // n, rounds * (j + 1) // n
+        part = []
+        for src, off, nbytes in sources:
+            a, e = min(nbytes, r0 * chunk), min(nbytes, r1 * chunk)
+            if e > a:
+                part.append((src + a, off + a, e - a))
+        parts.append(part)
+    return parts
+
+
 def measure_prefetch(layer, block, step, args, cfg, ms_block, engine_name):
     """Copy of the next layer's non-local experts into slot set 2: alone, and beside the block.
 
@@ -615,21 +632,11 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block, engine_name):
 
     chunk = int(args.chunk_mib * (1 << 20)) if args.chunk_mib else cfg.chunk_bytes
 
-    # Paced release (--burst-at): the plan's rounds are cut into equal parts, part j released when the
-    # block passes stage boundary bursts[j] (an event on the compute stream); each part is the same
-    # round-robin plan restricted to its rounds, so together they copy the same slices in the same order.
+    # Paced release (--burst-at): part j of the plan is released when the block passes stage boundary
+    # bursts[j] (an event on the compute stream).
     bursts = [int(v) for v in args.burst_at.split(",") if v != ""]
     assert all(0 <= v <= 4 for v in bursts), "--burst-at takes stage boundaries 0..4"
-    rounds = max(-(-s[2] // chunk) for s in layer.sources)
-    parts = []
-    for j in range(len(bursts)):
-        r0, r1 = rounds * j // len(bursts), rounds * (j + 1) // len(bursts)
-        part = []
-        for src, off, n in layer.sources:
-            a, e = min(n, r0 * chunk), min(n, r1 * chunk)
-            if e > a:
-                part.append((src + a, off + a, e - a))
-        parts.append(part)
+    parts = burst_parts(layer.sources, chunk, len(bursts)) if bursts else []
 
     def copy(wait=None, done=None, sources=None):
         # stream i copies source regions i, i + n, ...; the other streams join cs before `done`

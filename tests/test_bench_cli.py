@@ -36,3 +36,28 @@ def test_options_parse(monkeypatch):
     assert a.workload == "prefill16k_fp8" and a.copy_engine == "sdma"
     assert (a.copy_workgroups, a.copy_streams, a.chunk_mib, a.pipeline_layers) == (24, 2, 1.0, 3)
     assert a.shape_study and a.no_cpu_baseline and not a.no_prefetch
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_burst_parts_are_the_plan_cut_by_rounds(seed):
+    """--burst-at releases parts of the slice plan; planned one after another they must give exactly the
+    oracle's round-robin plan of the whole copy (same slices, same order)."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    from oracle.prefetch import chunk_plan
+    rng = np.random.default_rng(seed)
+    chunk = int(rng.choice([16, 48, 4096]))
+    n_src = int(rng.integers(1, 5))
+    sizes = [int(rng.integers(0, 20 * chunk)) for _ in range(n_src)]
+    bases = [0x100000 * (s + 1) for s in range(n_src)]
+    offs = list(np.cumsum([0] + sizes[:-1]))
+    sources = [(b, int(o), n) for b, o, n in zip(bases, offs, sizes)]
+
+    def plan(srcs):
+        return [(srcs[s][0] + so, do, ln) for s, so, do, ln in chunk_plan([x[2] for x in srcs], [x[1] for x in srcs],
+                                                                            chunk)]
+    whole = plan(sources)
+    for n in (1, 2, 3, 5):
+        got = [sl for part in bench.burst_parts(sources, chunk, n) for sl in plan(part)]
+        assert got == whole, (n, sizes, chunk)
