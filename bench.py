@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--burst-at", default="",
                     help="paced prefetch: comma-separated stage boundaries (0 block start, 1 after route, 2 after "
                          "permute, 3 after GEMM1, 4 after GEMM2) at which equal parts of the slice plan are released")
+    ap.add_argument("--occupancy-probe", action="store_true",
+                    help="time the block beside idle spinning workgroups (torch.cuda._sleep) that only occupy "
+                         "compute units: 1, 4 and 16 of them for the block's length, and 1 for a quarter of it")
     ap.add_argument("--copy-streams", type=int, default=1,
                     help="deal the prefetch's source regions round-robin over this many copy streams (the kernel "
                          "engine splits --copy-workgroups between them)")
@@ -362,6 +365,8 @@ def run_workload(cfg, args, steps, warmup, main):
         res["merge_ablation"] = measure_merge(layer, block, cfg, b, stage_ms)
     if main and args.shape_study:
         res["shape_study"] = measure_shapes(layer, block, cfg, b)
+    if main and args.occupancy_probe:
+        res["occupancy_probe"] = measure_occupancy(step, cfg)
     del layer, block, b, table
     torch.cuda.synchronize()
     return res
@@ -714,6 +719,47 @@ def measure_prefetch(layer, block, step, args, cfg, ms_block, engine_name):
                                                                                  zip(t_blk, t_cp)])),
                 slowdown=beside / alone - 1.0, hidden=bool(cbeside <= beside), reps=reps, record_check=ok,
                 note="stand-in source regions sit in the same HBM, so the copy reads and writes locally")
+
+
+def measure_occupancy(step, cfg, reps=8):
+    """The block beside workgroups that do nothing but occupy compute units.
+
+    torch.cuda._sleep launches one single-thread workgroup that spins for a number of GPU clock cycles and
+    touches no memory.  n of them go on n side streams, started with the block (the streams wait on the
+    block's first event); the block is timed with the single-step protocol of the prefetch leg.  Their
+    cost is what any concurrent kernel costs the block by its presence on the compute units alone."""
+    import torch
+
+    comp = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in range(16)]
+
+    def single(n, cycles):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record(comp)
+        for st in streams[:n]:
+            st.wait_event(ev[0])
+            with torch.cuda.stream(st):
+                torch.cuda._sleep(cycles)
+        step(ev)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[5])
+
+    alone = float(np.median([single(0, 0) for _ in range(reps)]))
+    # calibrate the spin: cycles per millisecond of the clock _sleep counts
+    probe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    probe[0].record(comp)
+    torch.cuda._sleep(10_000_000)
+    probe[1].record(comp)
+    torch.cuda.synchronize()
+    per_ms = 10_000_000 / max(probe[0].elapsed_time(probe[1]), 1e-3)
+    out = dict(block_ms_alone=alone, sleep_cycles_per_ms=per_ms, cases=[])
+    for n, frac in ((1, 1.2), (4, 1.2), (16, 1.2), (1, 0.25)):
+        ms = alone * frac
+        t = float(np.median([single(n, int(ms * per_ms)) for _ in range(reps)]))
+        out["cases"].append(dict(workgroups=n, spin_ms=ms, block_ms=t, slowdown=t / alone - 1.0))
+        log(f"{cfg.name}: block beside {n} idle workgroup(s) spinning {ms:.1f} ms: {alone:.3f} -> {t:.3f} ms "
+            f"({t / alone - 1:+.1%})")
+    return out
 
 
 def measure_smi(layer, step, args, cfg, secs=2.5):
