@@ -297,6 +297,62 @@ def fp8_output_not_rounded():
     m.expert_ffn_parts = parts
 
 
+def e4m3_subnormals_flushed():
+    c = _codecs()
+    orig = c.e4m3_encode
+
+    def enc(x):
+        x = np.asarray(x, np.float64)
+        code = orig(x)
+        small = np.abs(x) < 2.0 ** -6                 # below the smallest normal: flushed to a signed zero
+        return np.where(small & ~np.isnan(x), (np.signbit(x) * 0x80).astype(np.uint8), code).astype(np.uint8)
+    _set_codec("e4m3_encode", enc)
+
+
+def combine_rounds_each_term():
+    m = _moe()
+
+    def combine(y_rows, w, shared_row=None, precision="f32"):
+        y = np.asarray(y_rows, np.float64)
+        terms = [float(w[j]) * y[j] for j in range(len(w))]
+        if precision in ("bf16", "fp8"):
+            terms = [m.bf16_round(t) for t in terms]   # a rounding per term instead of one at the end
+        acc = np.zeros(y.shape[1:], np.float64)
+        for t in terms:
+            acc = acc + t
+        if shared_row is not None:
+            acc = acc + np.asarray(shared_row, np.float64)
+        if precision in ("bf16", "fp8"):
+            acc = m.bf16_round(acc)
+        return acc
+    m.combine = combine
+
+
+def bf16_expert_output_not_rounded():
+    m = _moe()
+    orig = m.expert_ffn_parts
+
+    def parts(X, wg, wu, wd, precision):
+        r = orig(X, wg, wu, wd, precision)
+        if precision == "bf16":
+            r["Y"] = np.asarray(r["A"], np.float64) @ np.asarray(wd, np.float64).T
+        return r
+    m.expert_ffn_parts = parts
+
+
+def fp8_token_groups_64():
+    m = _moe()
+
+    def qg(v):
+        v32 = np.asarray(v, np.float32)
+        n, K = v32.shape
+        g = v32.reshape(n, K // 64, 64)                 # 64-wide groups instead of 128
+        s = m._fp32_scale(np.abs(g).max(axis=2))
+        q = m.e4m3_encode((g / s[:, :, None]).astype(np.float32)).reshape(n, K)
+        return q, s[:, ::2]
+    m.quantize_groups = qg
+
+
 MUTANTS = {f.__name__: f for f in [
     silu_sign, swiglu_gate_up_swapped, swiglu_up_dropped, bf16_intermediate_not_rounded,
     combine_shared_dropped, combine_unweighted, combine_weights_reversed,
@@ -305,6 +361,7 @@ MUTANTS = {f.__name__: f for f in [
     bf16_truncates, e4m3_ties_away_from_zero, e4m3_overflow_to_nan, fp8_scale_uses_fnuz_max,
     fp8_block_amax_wrong_axes, fp8_a_not_requantised, fp8_scale_divisor_447, fp8_output_not_rounded,
     prefetch_source_major, prefetch_last_slice_full,
+    e4m3_subnormals_flushed, combine_rounds_each_term, bf16_expert_output_not_rounded, fp8_token_groups_64,
 ]}
 
 

@@ -382,3 +382,13 @@ def test_fp8_expert_against_torch_float8():
     ulp = np.abs(y) * 2.0 ** -7
     assert np.all(np.abs(parts["Y"] - y) <= ulp)          # equal up to one bf16 step (fp64 sum order)
     assert np.mean(parts["Y"] == y) > 0.99
+
+
+def test_combine_rounds_once_after_the_sum():
+    """The combine sums the weighted rows and rounds once (bf16 policy): worked by hand.
+    w = [2^-2 + 3*2^-11, 2^-1 + 2^-10] on two rows of ones.  The exact sum is 0.75244140625, above the
+    midpoint 0.751953125 between the bf16 neighbours 0.75 and 0.75390625, so it rounds to 0.75390625.
+    Rounding each term first (0.25146484375 -> 0.251953125, 0.5009765625 -> 0.5) would give 0.751953125,
+    a tie that rounds to the even 0.75."""
+    y = moe.combine(np.array([[1.0], [1.0]]), np.array([0.25146484375, 0.5009765625], np.float32), None, "bf16")
+    assert y.tolist() == [0.75390625]
