@@ -74,7 +74,126 @@ def parse():
                          "contiguous operands of the same shapes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run the slice-copy kernel on BYTES bytes (HBM counter calibration) and exit")
+    ap.add_argument("--operand-probe", action="store_true",
+                    help="only run the library's operand-stream probe (global_load_lds into an LDS ring, one "
+                         "512-thread workgroup per compute unit) over L2 hits, last-level-cache hits and HBM, "
+                         "print one JSON line and exit")
+    ap.add_argument("--tile-trace", action="store_true",
+                    help="only trace the workload's two expert-GEMM launches tile by tile and print their "
+                         "timeline statistics as one JSON line (needs a library built with "
+                         "-DDWDP_TILE_TRACE=1, loaded through DWDP_LIBRARY)")
     return ap.parse_args()
+
+
+def operand_probe(reps=4):
+    """Rates of the operand path (dwdp_diag_operand_stream) for each source of bytes, best of `reps`."""
+    import torch
+
+    from split_weight_expert_amd import api
+    MiB = 1 << 20
+    grid_full = 256
+    buf = torch.ones(16 << 30, dtype=torch.uint8, device="cuda")
+    # (name, span, stride, iters, grid, in_flight, cpol)
+    cases = [
+        ("L2 hits: every workgroup reads the same 1 MiB", MiB, 0, 200, grid_full, 3, 0),
+        ("last-level-cache hits: 256 regions of 1 MiB, each read 200 times", MiB, MiB, 200, grid_full, 3, 0),
+        ("HBM: 256 streams of 64 MiB, 3 steps in flight", 64 * MiB, 64 * MiB, 1, grid_full, 3, 0),
+        ("HBM: the same, non-temporal loads", 64 * MiB, 64 * MiB, 1, grid_full, 3, 2),
+        ("HBM: 5 steps in flight", 64 * MiB, 64 * MiB, 1, grid_full, 5, 0),
+        ("HBM: 2 steps in flight", 64 * MiB, 64 * MiB, 1, grid_full, 2, 0),
+        ("HBM: 1 step in flight", 64 * MiB, 64 * MiB, 1, grid_full, 1, 0),
+        ("HBM: 128 workgroups (half the compute units), 128 MiB each", 128 * MiB, 128 * MiB, 1, 128, 3, 0),
+        ("L2 hits: 1 step in flight", MiB, 0, 200, grid_full, 1, 0),
+    ]
+    out = []
+    for name, span, stride, iters, grid, infl, cpol in cases:
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            api.diag_operand_stream(buf, span, stride, iters, grid, infl, cpol)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        nbytes = span * iters * grid
+        row = dict(case=name, workgroups=grid, in_flight_steps=infl, step_bytes=32768, cpol=cpol, bytes=nbytes,
+                   ms=best, gbps_total=nbytes / best / 1e6, gbps_per_workgroup=nbytes / grid / best / 1e6)
+        log(f"{name}: {row['gbps_total']:.0f} GB/s ({row['gbps_per_workgroup']:.1f} per workgroup)")
+        out.append(row)
+    print(json.dumps(dict(operand_probe=out, note="best of %d launches, HIP events" % reps)), flush=True)
+
+
+def tile_trace(cfg, warm=3):
+    """Per-tile timeline of the two expert-GEMM launches of one block (tile-trace build)."""
+    import torch
+
+    from split_weight_expert_amd import api
+    from split_weight_expert_amd.workload import DeviceLayer
+    if "tile-trace=1" not in api.version():
+        print(f"bench.py --tile-trace: {api.version()!r} is not a tile-trace build (build one with "
+              "DWDP_EXTRA_FLAGS=-DDWDP_TILE_TRACE=1 split_weight_expert_amd/build.py --out ..., then set "
+              "DWDP_LIBRARY)", file=sys.stderr)
+        sys.exit(2)
+    layer = DeviceLayer(cfg, torch.device("cuda:0"), sources=False, slot_sets=2)
+    block, table = layer.block(), layer.table(1)
+    b = block.buffers(cfg.T)
+    def blocks(n):
+        for _ in range(n):
+            block.route(layer.x, layer.w_router, layer.bias, b)
+            block.permute(layer.x, b)
+            block.ffn(table, b)
+            block.combine(b)
+
+    blocks(warm)
+    torch.cuda.synchronize()
+    counts = np.diff(b.offsets.cpu().numpy().astype(np.int64))
+    res = dict(workload=cfg.name, tick_ns=10)
+    n_cu = 256
+    for stage in (1, 2):
+        # the traced launch follows busy blocks with no host wait between them, so that it runs at the
+        # clock the block holds; the clear sits between them on the stream
+        blocks(warm)
+        api.diag_tile_trace_clear()
+        block.ffn_stage(stage, table, b)
+        torch.cuda.synchronize()
+        tr = api.diag_tile_trace_read()
+        bid = np.nonzero(tr["t_end"] > 0)[0]
+        tr = tr[bid]
+        t0 = int(tr["t_start"].min())
+        st = (tr["t_start"] - t0) / 100.0            # 100 MHz counter -> us
+        en = (tr["t_end"] - t0) / 100.0
+        dur = en - st
+        span = float(en.max())
+        ma = (tr["rows"] + 31) // 32
+        full = ma == ma.max()
+        edges = np.arange(0.0, span + 10.0, 10.0)
+        running = np.array([int(((st <= t) & (en > t)).sum()) for t in edges])
+        inner = (edges >= 100.0) & (edges <= span - 100.0)
+        busy_tail = edges[running >= n_cu - 6]
+        clusters = tr["order"] // 32
+        spread = []
+        for c in np.unique(clusters):
+            m = clusters == c
+            if m.sum() == 32:
+                spread.append(float(st[m].max() - st[m].min()))
+        q = lambda a: [round(float(np.percentile(a, x)), 1) for x in (10, 50, 90)] if len(a) else None
+        res[f"gemm{stage}"] = dict(
+            tiles=int(len(tr)), span_us=round(span, 1),
+            full_tile_us=round(float(dur[full].mean()), 1), full_tiles=int(full.sum()),
+            one_block_tile_us=round(float(dur[ma == 1].mean()), 1) if (ma == 1).any() else None,
+            tile_us_by_active_blocks={int(m): [int((ma == m).sum()), round(float(dur[ma == m].mean()), 1)]
+                                      for m in np.unique(ma)},
+            cu_busy_mean=round(float(dur.sum() / (n_cu * span)), 3),
+            cu_busy_inside_100us=round(float(running[inner].mean() / n_cu), 3) if inner.any() else None,
+            tail_below_250_tiles_us=round(span - float(busy_tail.max()), 1) if len(busy_tail) else None,
+            xcd_end_us=[round(float(en[tr["xcd"] == x].max()), 1) if (tr["xcd"] == x).any() else None
+                        for x in range(8)],
+            xcd_is_workgroup_mod_8=round(float((tr["xcd"] == bid % 8).mean()), 4),
+            cluster_start_spread_us_p10_50_90=q(spread),
+            single_mtile_group_tiles=int((tr["group_m_tiles"] == 1).sum()),
+            rows_of_groups_traced=int(counts[np.unique(tr["group"])].sum()))
+        log(f"GEMM{stage}: {res[f'gemm{stage}']}")
+    print(json.dumps(dict(tile_trace=res, version=api.version())), flush=True)
 
 
 def calibrate_copy(nbytes, reps=3):
@@ -238,7 +357,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.operand_probe:
+        operand_probe()
+        return
     cfg = synth.get_config(args.workload)
+    if args.tile_trace:
+        tile_trace(cfg)
+        return
     res = run_workload(cfg, args, args.steps, args.warmup, main=True)
     legs = [w for w in args.legs.split(",") if w and w != cfg.name]
     if legs:

@@ -303,6 +303,47 @@ const char* dwdp_last_error(void);
 /* Library version string. */
 const char* dwdp_version(void);
 
+/* ---------------------------------------------------------------- diagnostics
+ * Measurements of the machine and of the expert GEMM's schedule.  They are not
+ * steps of the MoE block, and nothing on its path calls them. */
+
+/* Operand-stream probe: the rate at which workgroups move bytes from device memory into LDS
+ * with global_load_lds, the path every operand of the expert GEMM takes.  `grid` workgroups of
+ * 512 threads (one per compute unit at grid <= 256); workgroup b reads the `span` bytes at
+ * src + b*stride, `iters` times, in 32 KB steps (8 waves x 4 KB) into a ring of five 32 KB LDS
+ * slots, keeping `in_flight` steps (1..5) outstanding.  cpol 0 is the default cache policy, 2
+ * non-temporal.  stride 0 makes every workgroup read the same bytes (L2 hits once warm).
+ * The caller guarantees that src holds (grid-1)*stride + span bytes (the library cannot see
+ * the allocation).  span: a positive multiple of 32768; 1 <= grid <= 65536; iters >= 1.
+ * Reads only; time it with events on `stream`. */
+int dwdp_diag_operand_stream(const void* src, size_t span, size_t stride, int iters, int grid,
+                             int in_flight, int cpol, void* stream);
+
+/* Tile trace of the expert GEMM (bf16 and fp8 paths).  A library built with
+ * -DDWDP_TILE_TRACE=1 has every workgroup of an expert-GEMM launch write one record into a fixed
+ * device array of 131072 records, at the workgroup's index: its tile, the XCD it ran on and the
+ * GPU's real-time counter (100 MHz) when it started and when its last wave finished.  Clear the
+ * array, run ONE grouped-FFN stage, synchronise, read.  Slots of workgroups that ran no tile (or
+ * beyond the array) keep t_end == 0.  Other builds return DWDP_ERR_UNSUPPORTED. */
+typedef struct {
+    uint64_t t_start;           /* real-time counter when the workgroup took its tile */
+    uint64_t t_end;             /* ... and after its last wave finished the tile */
+    int32_t order;              /* the tile's position in the schedule */
+    int32_t group;              /* expert group */
+    int32_t first_row;          /* first permuted row of the tile */
+    int32_t rows;               /* rows of the tile */
+    int32_t n_tile;             /* 256-column output tile (GEMM1: 128 gate + 128 up columns) */
+    int32_t group_m_tiles;      /* m-tiles of the group */
+    int32_t xcd;                /* XCD the workgroup ran on */
+    int32_t reserved_;
+} dwdp_tile_record;
+
+/* Zero the trace array on the current device (stream ordered). */
+int dwdp_diag_tile_trace_clear(void* stream);
+/* Copy the first min(max_records, 131072) records of the current device's array to host memory
+ * `out` (synchronous: waits for the device) and store that count in *n_records. */
+int dwdp_diag_tile_trace_read(dwdp_tile_record* out, size_t max_records, size_t* n_records);
+
 #ifdef __cplusplus
 }
 #endif

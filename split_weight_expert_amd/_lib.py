@@ -31,6 +31,13 @@ class Chunk(ctypes.Structure):
                 ("dst_offset", ctypes.c_size_t), ("bytes", ctypes.c_size_t)]
 
 
+class TileRecord(ctypes.Structure):
+    _fields_ = [("t_start", ctypes.c_uint64), ("t_end", ctypes.c_uint64), ("order", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("first_row", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("n_tile", ctypes.c_int32), ("group_m_tiles", ctypes.c_int32), ("xcd", ctypes.c_int32),
+                ("reserved_", ctypes.c_int32)]
+
+
 class DwdpError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"dwdp error {code}: {msg}")
@@ -62,6 +69,9 @@ SIGNATURES = {
     "dwdp_pack_weights": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "dwdp_quantize_weight_fp8": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "dwdp_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "dwdp_diag_operand_stream": (_i32, [_vp, _sz, _sz, _i32, _i32, _i32, _i32, _vp]),
+    "dwdp_diag_tile_trace_clear": (_i32, [_vp]),
+    "dwdp_diag_tile_trace_read": (_i32, [_vp, _sz, ctypes.POINTER(_sz)]),
     "dwdp_last_error": (ctypes.c_char_p, []),
     "dwdp_version": (ctypes.c_char_p, []),
 }

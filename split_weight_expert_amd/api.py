@@ -183,3 +183,32 @@ def pack_weights(w, out, dtype_code_, stream=None):
     """Re-lay a weight matrix w [N, K] (bf16, or uint8 E4M3 codes) into the fragment-major layout in out."""
     N, K = w.shape
     _lib.check(_lib.load().dwdp_pack_weights(_ptr(w), N, K, dtype_code_, _ptr(out), _stream(stream)))
+
+
+# ------------------------------------------------------------------ diagnostics (not steps of the block)
+
+def diag_operand_stream(src, span, stride, iters, grid, in_flight=3, cpol=0, stream=None):
+    """Operand-stream probe over the uint8 device tensor src: grid workgroups each read span bytes at
+    b*stride, iters times, into an LDS ring with in_flight 32 KB steps outstanding."""
+    need = (grid - 1) * stride + span
+    if src.dtype != torch.uint8 or not src.is_cuda or src.numel() < need:
+        raise ValueError(f"src must be a uint8 device tensor of at least {need} bytes")
+    _lib.check(_lib.load().dwdp_diag_operand_stream(_ptr(src), span, stride, iters, grid, in_flight, cpol,
+                                                    _stream(stream)))
+
+
+def diag_tile_trace_clear(stream=None):
+    _lib.check(_lib.load().dwdp_diag_tile_trace_clear(_stream(stream)))
+
+
+def diag_tile_trace_read(max_records=1 << 17):
+    """Tile records of the last expert-GEMM launch as a numpy structured array (tile-trace builds)."""
+    import numpy as np
+    buf = (_lib.TileRecord * max_records)()
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().dwdp_diag_tile_trace_read(buf, max_records, ctypes.byref(n)))
+    dt = np.dtype([("t_start", "<u8"), ("t_end", "<u8"), ("order", "<i4"), ("group", "<i4"), ("first_row", "<i4"),
+                   ("rows", "<i4"), ("n_tile", "<i4"), ("group_m_tiles", "<i4"), ("xcd", "<i4"),
+                   ("reserved_", "<i4")])
+    assert dt.itemsize == ctypes.sizeof(_lib.TileRecord)
+    return np.frombuffer(bytes(buf)[: n.value * dt.itemsize], dtype=dt).copy()

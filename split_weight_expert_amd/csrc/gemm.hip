@@ -31,7 +31,21 @@
 #include "common.h"
 #include "internal.h"
 
+// Tile trace (a diagnostic): built with -DDWDP_TILE_TRACE=1, every workgroup of gemm_frag_kernel stores
+// one dwdp_tile_record -- its tile, its XCD and the real-time counter at its start and end -- at its
+// index in a fixed device array, which dwdp_diag_tile_trace_clear / _read zero and read.  The default
+// build compiles none of it.
+#ifndef DWDP_TILE_TRACE
+#define DWDP_TILE_TRACE 0
+#endif
+
 namespace dwdp {
+
+#if DWDP_TILE_TRACE
+constexpr int kTraceRecords = 1 << 17;
+static __device__ dwdp_tile_record tile_trace[kTraceRecords];
+#endif
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -77,6 +91,9 @@ struct Tile {
     int64_t row0;
     int nrows;
     int mc;       // m-tiles of the group (1: the tile is the only reader of its weight slab)
+#if DWDP_TILE_TRACE
+    int lin;      // position in the schedule
+#endif
 };
 
 // Row of the activation matrix that holds permuted row prow: itself, or its token (clamped).
@@ -118,6 +135,9 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
     const int slot = bid / kNumXcd;
     const int lin = ((slot / kCluster) * kNumXcd + bid % kNumXcd) * kCluster + slot % kCluster;
     if (lin >= total) return false;
+#if DWDP_TILE_TRACE
+    t.lin = lin;
+#endif
     if (KIND == kRouter) {
         const int mi = lin % mt_router;
         t.g = 0;
@@ -1041,6 +1061,9 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
 
     TileCtx c;
     if (!decode_tile<BM, KIND>(p, c.t)) return;
+#if DWDP_TILE_TRACE
+    const uint64_t trace_t0 = __builtin_amdgcn_s_memrealtime();
+#endif
     // Above the default wave priority, so that the GEMM's waves win the arbitration on a CU that also
     // hosts waves of another kernel (the layer-ahead prefetch copy); alone it makes no difference.
     __builtin_amdgcn_s_setprio(2);
@@ -1121,6 +1144,23 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
         if (c.t.mc == 1) dispatch(std::integral_constant<int, kStreamWeightCpol>{});
         else dispatch(std::integral_constant<int, DWDP_WEIGHT_CPOL>{});
     }
+#if DWDP_TILE_TRACE
+    __syncthreads();                                   // every wave has finished the tile
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kTraceRecords) {
+        dwdp_tile_record r;
+        r.t_start = trace_t0;
+        r.t_end = __builtin_amdgcn_s_memrealtime();
+        r.order = c.t.lin;
+        r.group = c.t.g;
+        r.first_row = (int32_t)c.t.row0;
+        r.rows = c.t.nrows;
+        r.n_tile = c.t.nt;
+        r.group_m_tiles = c.t.mc;
+        r.xcd = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xF);   // hardware register XCC_ID, bits 3:0
+        r.reserved_ = 0;
+        tile_trace[blockIdx.x] = r;
+    }
+#endif
 }
 
 // ------------------------------------------------------------------------------ weight packing
@@ -1496,6 +1536,48 @@ extern "C" int dwdp_moe_grouped_ffn(const dwdp_expert_ptrs* table, int n_groups,
                                     int w_dtype, void* y_perm, void* ws, size_t ws_bytes, void* stream) {
     return dwdp_moe_grouped_ffn_stage(0, table, n_groups, offsets, x_perm, x_perm_scale, rows, H, I, w_dtype, y_perm,
                                       ws, ws_bytes, stream);
+}
+
+#if DWDP_TILE_TRACE
+namespace {
+__global__ __launch_bounds__(256) void zero_trace_kernel(uint4* __restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = uint4{0, 0, 0, 0};
+}
+}  // namespace
+#endif
+
+extern "C" int dwdp_diag_tile_trace_clear(void* stream) {
+    clear_error();
+#if DWDP_TILE_TRACE
+    void* p = nullptr;
+    DWDP_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(tile_trace)));
+    static_assert(sizeof(tile_trace) % 16 == 0, "whole 16-byte words");
+    const int64_t n = (int64_t)(sizeof(tile_trace) / 16);
+    hipLaunchKernelGGL(zero_trace_kernel, dim3(1024), dim3(256), 0, as_stream(stream), static_cast<uint4*>(p), n);
+    DWDP_LAUNCHED();
+    return DWDP_OK;
+#else
+    (void)stream;
+    return fail(DWDP_ERR_UNSUPPORTED, "dwdp_diag_tile_trace_clear: the library was built without -DDWDP_TILE_TRACE=1");
+#endif
+}
+
+extern "C" int dwdp_diag_tile_trace_read(dwdp_tile_record* out, size_t max_records, size_t* n_records) {
+    clear_error();
+    DWDP_REQUIRE(out != nullptr && n_records != nullptr, "null pointer argument");
+#if DWDP_TILE_TRACE
+    void* p = nullptr;
+    DWDP_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(tile_trace)));
+    const size_t n = std::min(max_records, (size_t)kTraceRecords);
+    DWDP_HIP(hipDeviceSynchronize());
+    DWDP_HIP(hipMemcpy(out, p, n * sizeof(dwdp_tile_record), hipMemcpyDeviceToHost));
+    *n_records = n;
+    return DWDP_OK;
+#else
+    (void)max_records;
+    return fail(DWDP_ERR_UNSUPPORTED, "dwdp_diag_tile_trace_read: the library was built without -DDWDP_TILE_TRACE=1");
+#endif
 }
 
 extern "C" int dwdp_pack_weights(const void* w, int64_t N, int64_t K, int dtype, void* out, void* stream) {

@@ -157,6 +157,9 @@ const char* dwdp_version(void) {
 #ifdef DWDP_YPERM_NT
            " yperm-nt=" DWDP_STR(DWDP_YPERM_NT)
 #endif
+#ifdef DWDP_TILE_TRACE
+           " tile-trace=" DWDP_STR(DWDP_TILE_TRACE)
+#endif
 #ifdef DWDP_COMBINE_NT
            " combine-nt=" DWDP_STR(DWDP_COMBINE_NT)
 #endif

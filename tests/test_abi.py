@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lib_mod.SIGNATURES), "binding signatures and header disagree"
@@ -212,3 +212,29 @@ def test_launch_sizes_beyond_one_dispatch_are_rejected(lib):
     rows = (1 << 31) - 1
     expect(E_, lib.dwdp_moe_grouped_ffn(FAKE, 1, FAKE, FAKE, None, rows, 256, 128, 1, FAKE, FAKE, 1 << 62, None), lib,
            "too large")
+
+
+def test_diagnostics_reject_bad_arguments_and_the_default_build_has_no_tile_trace(lib):
+    f = lib.dwdp_diag_operand_stream
+    E_ = lib_mod.DWDP_ERR_INVALID_ARG
+    MiB = 1 << 20
+    expect(E_, f(None, MiB, 0, 1, 1, 3, 0, None), lib, "NULL")
+    expect(E_, f(ODD, MiB, 0, 1, 1, 3, 0, None), lib, "aligned")
+    expect(E_, f(FAKE, MiB + 16, 0, 1, 1, 3, 0, None), lib, "32768")
+    expect(E_, f(FAKE, 0, 0, 1, 1, 3, 0, None), lib, "32768")
+    expect(E_, f(FAKE, MiB, 8, 1, 1, 3, 0, None), lib, "stride")
+    expect(E_, f(FAKE, MiB, 0, 0, 1, 3, 0, None), lib, "iters")
+    expect(E_, f(FAKE, MiB, 0, 1, 0, 3, 0, None), lib, "grid")
+    expect(E_, f(FAKE, MiB, 0, 1, 65537, 3, 0, None), lib, "grid")
+    expect(E_, f(FAKE, MiB, 0, 1, 1, 0, 0, None), lib, "in_flight")
+    expect(E_, f(FAKE, MiB, 0, 1, 1, 6, 0, None), lib, "in_flight")
+    expect(E_, f(FAKE, MiB, 0, 1, 1, 3, 1, None), lib, "cpol")
+    assert ctypes.sizeof(lib_mod.TileRecord) == 48
+    n = ctypes.c_size_t(7)
+    buf = (lib_mod.TileRecord * 4)()
+    expect(E_, lib.dwdp_diag_tile_trace_read(None, 4, ctypes.byref(n)), lib, "null")
+    if b"tile-trace=1" not in lib.dwdp_version():
+        U = lib_mod.DWDP_ERR_UNSUPPORTED
+        expect(U, lib.dwdp_diag_tile_trace_clear(None), lib, "DWDP_TILE_TRACE")
+        expect(U, lib.dwdp_diag_tile_trace_read(buf, 4, ctypes.byref(n)), lib, "DWDP_TILE_TRACE")
+        assert n.value == 7

@@ -1,0 +1,117 @@
+"""The library's diagnostics on the GPU: the operand-stream probe, and the expert GEMM's tile trace.
+
+The tile trace is compiled in only with -DDWDP_TILE_TRACE=1; its test loads such a build
+(split_weight_expert_amd/lib/trace/libdwdp.so, made by split_weight_expert_amd/build.py --out) and
+checks that the traced launch ran every tile of the schedule exactly once and that the trace build
+computes the default build's results bit for bit.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import need_gpu
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TRACE_LIB = os.path.join(ROOT, "split_weight_expert_amd", "lib", "trace", "libdwdp.so")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def test_operand_stream_probe_runs_every_configuration():
+    from split_weight_expert_amd import api
+    span, grid = 64 << 10, 4
+    buf = torch.ones(grid * span, dtype=torch.uint8, device=DEV)
+    for in_flight in range(1, 6):
+        for cpol in (0, 2):
+            api.diag_operand_stream(buf, span, span, 2, grid, in_flight, cpol)
+            api.diag_operand_stream(buf, span, 0, 3, grid, in_flight, cpol)
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError):
+        api.diag_operand_stream(buf, span, span, 1, grid + 1)        # would read past the tensor
+
+
+def _problem(dt, counts, H, I, seed):
+    from split_weight_expert_amd import ExpertStore, api
+    from split_weight_expert_amd.moe import DTYPES
+    rng = np.random.default_rng(seed)
+    G = len(counts)
+    rows = int(sum(counts))
+    store = ExpertStore(H, I, DTYPES[dt], [G], device=DEV)
+    for g in range(G):
+        w = [torch.from_numpy(rng.standard_normal(s).astype(np.float32) / np.sqrt(s[1])).to(DEV)
+             for s in ((I, H), (I, H), (H, I))]
+        store.load(0, g, *w)
+    table = store.table([(0, g) for g in range(G)], DEV)
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(DEV)
+    x = torch.from_numpy(rng.standard_normal((rows, H)).astype(np.float32)).to(DEV, torch.bfloat16)
+    if dt == "fp8":
+        xq = torch.empty(rows, H, dtype=torch.uint8, device=DEV)
+        xs = torch.empty(rows, H // 128, dtype=torch.float32, device=DEV)
+        api.quantize_tokens_fp8(x, xq, xs)
+        x, x_scale, wcode = xq, xs, api.FP8_E4M3
+    else:
+        x_scale, wcode = None, api.BF16
+    ws = torch.empty(api.workspace_bytes(api.OP_GROUPED_FFN, rows, 1, G, H, I, wcode, 0), dtype=torch.uint8,
+                     device=DEV)
+    return store, table, offsets, x, x_scale, wcode, ws, rows
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_tile_trace_covers_every_tile_once_and_changes_no_result(dt):
+    if not os.path.exists(TRACE_LIB):
+        pytest.skip("no tile-trace build (DWDP_EXTRA_FLAGS=-DDWDP_TILE_TRACE=1 split_weight_expert_amd/build.py "
+                    "--out split_weight_expert_amd/lib/trace/libdwdp.so)")
+    from split_weight_expert_amd import _lib, api
+    H, I = 512, 256
+    counts = [0, 3, 40, 300, 700, 64, 1, 257, 33]
+    G = len(counts)
+    store, table, offsets, x, x_scale, wcode, ws, rows = _problem(dt, counts, H, I, seed=5)
+    y_default = torch.empty(rows, H, dtype=torch.bfloat16, device=DEV)
+    api.moe_grouped_ffn_stage(0, table, G, offsets, x, x_scale, H, I, wcode, y_default, ws)
+    torch.cuda.synchronize()
+
+    saved = _lib._lib
+    _lib._lib = None
+    try:
+        _lib.load(TRACE_LIB)
+        assert "tile-trace=1" in api.version()
+        y_trace = torch.empty(rows, H, dtype=torch.bfloat16, device=DEV)
+        traces = {}
+        for stage in (1, 2):
+            api.diag_tile_trace_clear()
+            api.moe_grouped_ffn_stage(stage, table, G, offsets, x, x_scale, H, I, wcode, y_trace, ws)
+            torch.cuda.synchronize()
+            tr = api.diag_tile_trace_read(4096)
+            traces[stage] = tr[tr["t_end"] > 0]
+    finally:
+        _lib._lib = saved
+    assert torch.equal(y_trace, y_default), "the tile-trace build changed the results"
+
+    off = np.concatenate([[0], np.cumsum(counts)])
+    for stage, n_tiles in ((1, I // 128), (2, H // 256)):
+        tr = traces[stage]
+        assert (tr["t_end"] >= tr["t_start"]).all()
+        assert ((tr["xcd"] >= 0) & (tr["xcd"] < 8)).all()
+        assert len(np.unique(tr["order"])) == len(tr), "a schedule position ran twice"
+        for g in range(G):
+            mine = tr[tr["group"] == g]
+            if counts[g] == 0:
+                assert len(mine) == 0
+                continue
+            for nt in range(n_tiles):
+                cov = np.zeros(counts[g], np.int32)
+                for r in mine[mine["n_tile"] == nt]:
+                    lo = r["first_row"] - off[g]
+                    assert 0 <= lo and lo + r["rows"] <= counts[g] and r["rows"] > 0
+                    cov[lo:lo + r["rows"]] += 1
+                assert (cov == 1).all(), f"stage {stage} group {g} n-tile {nt}: rows covered {np.unique(cov)}"
+            assert set(mine["n_tile"].tolist()) == set(range(n_tiles))
+            assert (mine["group_m_tiles"] == len(np.unique(mine["first_row"]))).all()
