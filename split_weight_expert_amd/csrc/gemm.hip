@@ -83,6 +83,8 @@ struct GemmParams {
     int I;                          // GEMM1: first up row inside W13
     uint8_t* out;
     float* out_scale;               // GEMM1 fp8: A scales [rows, I/128]
+    int32_t* ticket;                // expert GEMMs: tile ticket counter (tiles drawn in schedule order), or
+                                    // null (tile fixed by the workgroup index, clusters dealt over the XCDs)
 };
 
 struct Tile {
@@ -121,8 +123,16 @@ constexpr int kCluster = 32;
 #define DWDP_MSUPER_BALANCED 0
 #endif
 
+// Schedule position of this workgroup's tile: workgroup b runs on XCD b % 8, and XCD x takes
+// clusters x, x+8, ... of kCluster consecutive positions.
+__device__ __forceinline__ int dealt_lin() {
+    const int bid = blockIdx.x;
+    const int slot = bid / kNumXcd;
+    return ((slot / kCluster) * kNumXcd + bid % kNumXcd) * kCluster + slot % kCluster;
+}
+
 template <int BM, int KIND>
-__device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
+__device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t, int lin) {
     int total;
     int mt_router = 0;
     if (KIND == kRouter) {
@@ -131,9 +141,6 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
     } else {
         total = p.mprefix[p.G] * p.NT;
     }
-    const int bid = blockIdx.x;
-    const int slot = bid / kNumXcd;
-    const int lin = ((slot / kCluster) * kNumXcd + bid % kNumXcd) * kCluster + slot % kCluster;
     if (lin >= total) return false;
 #if DWDP_TILE_TRACE
     t.lin = lin;
@@ -182,6 +189,11 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
     return true;
 }
 
+template <int BM, int KIND>
+__device__ __forceinline__ bool decode_tile(const GemmParams& p, Tile& t) {
+    return decode_tile<BM, KIND>(p, t, dealt_lin());
+}
+
 // ------------------------------------------------------------------------------ schedule
 // One workgroup: m-tile counts per group, their exclusive scan, and two m-tile tables over the same
 // tiles: `mtiles` in group order and `mtiles_by_size` with the groups taken by row count, largest
@@ -195,11 +207,17 @@ constexpr int kSortGroups = 4096;
 #ifndef DWDP_BALANCED_MTILES
 #define DWDP_BALANCED_MTILES 0
 #endif
+// 32-row tiles draw their schedule position from a ticket counter (0: dealt over the XCDs like the rest)
+#ifndef DWDP_TICKET_TILES
+#define DWDP_TICKET_TILES 1
+#endif
 
 template <int BM>
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int G,
                                                         int32_t* __restrict__ mprefix, MTile* __restrict__ mtiles,
-                                                        MTile* __restrict__ mtiles_by_size) {
+                                                        MTile* __restrict__ mtiles_by_size,
+                                                        int32_t* __restrict__ tickets) {
+    if (tickets != nullptr && threadIdx.x < 2) tickets[threadIdx.x] = 0;   // both launches' ticket counters
     __shared__ int wave_sum[16];
     __shared__ int carry_s;
     __shared__ int order_s[kSortGroups];
@@ -1060,7 +1078,26 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
     float* s_bscale = reinterpret_cast<float*>(smem + C::NS * C::STAGE);   // fp8 only
 
     TileCtx c;
-    if (!decode_tile<BM, KIND>(p, c.t)) return;
+    int lin;
+    if (p.ticket != nullptr) {
+        // Tiles in schedule order to whichever workgroup asks first, on any XCD (used where tiles share
+        // next to nothing: 32-row tiles of small groups, which only stream weights).  Every workgroup
+        // draws exactly one ticket, so the draw of ticket gridDim.x - 1 is the launch's last: that
+        // workgroup resets the counter for the next launch.  The ticket passes through the ring's first
+        // word, which is rewritten only after the second barrier.
+        int* s_ticket = reinterpret_cast<int*>(smem);
+        if (threadIdx.x == 0) {
+            const int tk = atomicAdd(p.ticket, 1);
+            if (tk == (int)gridDim.x - 1) atomicExch(p.ticket, 0);
+            *s_ticket = tk;
+        }
+        __syncthreads();
+        lin = *s_ticket;
+        __syncthreads();
+    } else {
+        lin = dealt_lin();
+    }
+    if (!decode_tile<BM, KIND>(p, c.t, lin)) return;
 #if DWDP_TILE_TRACE
     const uint64_t trace_t0 = __builtin_amdgcn_s_memrealtime();
 #endif
@@ -1288,8 +1325,9 @@ int choose_bm(int dtype, int64_t rows, int groups) {
 }
 
 template <int BM>
-void launch_schedule(const int32_t* offsets, int G, int32_t* pre, MTile* mt, MTile* mt_by_size, hipStream_t st) {
-    hipLaunchKernelGGL(schedule_kernel<BM>, dim3(1), dim3(1024), 0, st, offsets, G, pre, mt, mt_by_size);
+void launch_schedule(const int32_t* offsets, int G, int32_t* pre, MTile* mt, MTile* mt_by_size, int32_t* tickets,
+                     hipStream_t st) {
+    hipLaunchKernelGGL(schedule_kernel<BM>, dim3(1), dim3(1024), 0, st, offsets, G, pre, mt, mt_by_size, tickets);
 }
 
 // decode_tile deals clusters of kCluster tiles round-robin over the 8 XCDs, so the launch holds whole
@@ -1319,7 +1357,7 @@ void launch_dma(const GemmParams& p, int64_t tiles, hipStream_t st) {
 template <int BM>
 void launch_ffn(bool g1, bool g2, bool fp8_path, const int32_t* offsets, int G, const GemmParams& p1,
                 const GemmParams& p2, MTile* mt_group, MTile* mt_size, int64_t maxm, hipStream_t st) {
-    if (g1) launch_schedule<BM>(offsets, G, const_cast<int32_t*>(p1.mprefix), mt_group, mt_size, st);
+    if (g1) launch_schedule<BM>(offsets, G, const_cast<int32_t*>(p1.mprefix), mt_group, mt_size, p1.ticket, st);
 #ifdef DWDP_FP8_BM256
     constexpr bool fp8_tiles = true;
 #else
@@ -1438,12 +1476,20 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     p2.NT = w_dtype == DWDP_F32 ? H / kBnF32 : H / kBnDma;
     p2.out = static_cast<uint8_t*>(y_perm);
     p2.out_scale = nullptr;
+    // 32-row tiles (a few rows per group, as in decode) share next to nothing: they draw tickets, so
+    // that every XCD keeps taking tiles until none are left.  The schedule kernel zeroes both counters
+    // (p2.ticket = p1.ticket + 1), and each launch's last draw resets its own.
+    if (DWDP_TICKET_TILES && w_dtype != DWDP_F32 && bm == 32) {
+        p1.ticket = reinterpret_cast<int32_t*>(base + L.tickets);
+        p2.ticket = p1.ticket + 1;
+    }
     // every expert-GEMM launch holds at most 512 work-items per workgroup
     DWDP_REQUIRE(xcd_grid(maxm * std::max(p1.NT, p2.NT)) * 512 <= kMaxLaunchItems, "problem too large for one launch");
 
     const bool g1 = stage != 2, g2 = stage != 1;
     if (w_dtype == DWDP_F32) {
-        if (g1) launch_schedule<kBmF32>(offsets, n_groups, const_cast<int32_t*>(p1.mprefix), mt_group, mt_size, st);
+        if (g1) launch_schedule<kBmF32>(offsets, n_groups, const_cast<int32_t*>(p1.mprefix), mt_group, mt_size, nullptr,
+                                        st);
         if (g1) launch_f32<kGemm1>(p1, maxm * p1.NT, st);
         if (g2) launch_f32<kGemm2>(p2, maxm * p2.NT, st);
     } else {

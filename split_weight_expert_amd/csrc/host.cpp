@@ -61,6 +61,8 @@ FfnWs ffn_ws_layout(int64_t rows, int groups, int I, int dtype) {
     off += align256((size_t)maxm * kMTileBytes);
     w.mt_by_size = off;
     off += align256((size_t)maxm * kMTileBytes);
+    w.tickets = off;
+    off += align256(2 * sizeof(int32_t));
     w.total = off;
     return w;
 }
@@ -156,6 +158,9 @@ const char* dwdp_version(void) {
 #endif
 #ifdef DWDP_YPERM_NT
            " yperm-nt=" DWDP_STR(DWDP_YPERM_NT)
+#endif
+#ifdef DWDP_TICKET_TILES
+           " ticket-tiles=" DWDP_STR(DWDP_TICKET_TILES)
 #endif
 #ifdef DWDP_TILE_TRACE
            " tile-trace=" DWDP_STR(DWDP_TILE_TRACE)

@@ -30,10 +30,11 @@ inline int64_t hist_chunk(int64_t N) {
 inline int64_t hist_chunks(int64_t N) { return (N + hist_chunk(N) - 1) / hist_chunk(N); }
 
 // Grouped-FFN workspace: A [rows, I] in the activation type (+ its fp8 scales [rows, I/128]), the
-// m-tile prefix [G+1] and two m-tile tables, each part 256-byte aligned; the tables are sized for
-// the smallest tile height, so any tile choice fits.
+// m-tile prefix [G+1], two m-tile tables and the two expert-GEMM launches' tile tickets (int32 each),
+// each part 256-byte aligned; the tables are sized for the smallest tile height, so any tile choice
+// fits.
 struct FfnWs {
-    size_t a, a_scale, pre, mt, mt_by_size, total;
+    size_t a, a_scale, pre, mt, mt_by_size, tickets, total;
 };
 FfnWs ffn_ws_layout(int64_t rows, int groups, int I, int dtype);
 

@@ -64,14 +64,20 @@ def _problem(dt, counts, H, I, seed):
     return store, table, offsets, x, x_scale, wcode, ws, rows
 
 
-@pytest.mark.parametrize("dt", ["bf16", "fp8"])
-def test_tile_trace_covers_every_tile_once_and_changes_no_result(dt):
+# 128-row tiles dealt over the XCDs; and 32-row tiles drawn from the ticket counter (a few rows per group,
+# as in decode, one group of several m-tiles among them)
+COUNTS = {"dealt": [0, 3, 40, 300, 700, 64, 1, 257, 33],
+          "tickets": [2, 0, 5, 1, 7, 3, 100, 4, 0, 6, 1, 2, 33, 5, 3, 1, 0, 8, 2, 64]}
+
+
+@pytest.mark.parametrize("dt,mode", [("bf16", "dealt"), ("fp8", "dealt"), ("bf16", "tickets"), ("fp8", "tickets")])
+def test_tile_trace_covers_every_tile_once_and_changes_no_result(dt, mode):
     if not os.path.exists(TRACE_LIB):
         pytest.skip("no tile-trace build (DWDP_EXTRA_FLAGS=-DDWDP_TILE_TRACE=1 split_weight_expert_amd/build.py "
                     "--out split_weight_expert_amd/lib/trace/libdwdp.so)")
     from split_weight_expert_amd import _lib, api
     H, I = 512, 256
-    counts = [0, 3, 40, 300, 700, 64, 1, 257, 33]
+    counts = COUNTS[mode]
     G = len(counts)
     store, table, offsets, x, x_scale, wcode, ws, rows = _problem(dt, counts, H, I, seed=5)
     y_default = torch.empty(rows, H, dtype=torch.bfloat16, device=DEV)
@@ -85,7 +91,7 @@ def test_tile_trace_covers_every_tile_once_and_changes_no_result(dt):
         assert "tile-trace=1" in api.version()
         y_trace = torch.empty(rows, H, dtype=torch.bfloat16, device=DEV)
         traces = {}
-        for stage in (1, 2):
+        for stage in (1, 2, 2):     # stage 2 twice: the second launch finds its ticket counter reset
             api.diag_tile_trace_clear()
             api.moe_grouped_ffn_stage(stage, table, G, offsets, x, x_scale, H, I, wcode, y_trace, ws)
             torch.cuda.synchronize()
@@ -94,6 +100,8 @@ def test_tile_trace_covers_every_tile_once_and_changes_no_result(dt):
     finally:
         _lib._lib = saved
     assert torch.equal(y_trace, y_default), "the tile-trace build changed the results"
+    # tile heights: 32 rows where the tiles draw tickets, 128 where they are dealt
+    assert (traces[1]["rows"].max() <= 32) == (mode == "tickets")
 
     off = np.concatenate([[0], np.cumsum(counts)])
     for stage, n_tiles in ((1, I // 128), (2, H // 256)):
