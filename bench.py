@@ -76,8 +76,8 @@ def parse():
                     help="only run the slice-copy kernel on BYTES bytes (HBM counter calibration) and exit")
     ap.add_argument("--operand-probe", action="store_true",
                     help="only run the library's operand-stream probe (global_load_lds into an LDS ring, one "
-                         "512-thread workgroup per compute unit) over L2 hits, last-level-cache hits and HBM, "
-                         "print one JSON line and exit")
+                         "512-thread workgroup per compute unit) over L2 hits, last-level-cache hits and HBM, and "
+                         "its LDS read probe, print one JSON line and exit")
     ap.add_argument("--tile-trace", action="store_true",
                     help="only trace the workload's two expert-GEMM launches tile by tile and print their "
                          "timeline statistics as one JSON line (needs a library built with "
@@ -120,7 +120,15 @@ def operand_probe(reps=4):
                    ms=best, gbps_total=nbytes / best / 1e6, gbps_per_workgroup=nbytes / grid / best / 1e6)
         log(f"{name}: {row['gbps_total']:.0f} GB/s ({row['gbps_per_workgroup']:.1f} per workgroup)")
         out.append(row)
-    print(json.dumps(dict(operand_probe=out, note="best of %d launches, HIP events" % reps)), flush=True)
+    lds = []
+    for waves in (4, 8, 16):
+        for grid in (256, 1):
+            api.diag_lds_read(grid, waves, 2000)                     # warm-up
+            bpc, ghz = api.diag_lds_read(grid, waves, 20000)
+            lds.append(dict(waves_per_workgroup=waves, workgroups=grid, bytes_per_clock_per_cu=bpc, shader_ghz=ghz))
+            log(f"LDS reads, {waves} waves x {grid} workgroups: {bpc:.0f} B per clock per CU at {ghz:.2f} GHz")
+    print(json.dumps(dict(operand_probe=out, lds_read=lds, note="best of %d launches, HIP events; LDS rate from "
+                          "the shader-clock counter" % reps)), flush=True)
 
 
 def tile_trace(cfg, warm=3):

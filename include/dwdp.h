@@ -319,6 +319,16 @@ const char* dwdp_version(void);
 int dwdp_diag_operand_stream(const void* src, size_t span, size_t stride, int iters, int grid,
                              int in_flight, int cpol, void* stream);
 
+/* LDS read probe: `grid` workgroups of `waves` waves (4, 8 or 16) each read a 128 KB LDS array with
+ * ds_read_b128 (lane-consecutive 16-byte slots, so no bank conflicts; 16 reads in flight per wave)
+ * `iters` times 16 KB per wave.  Thread 0 of workgroup b stores the shader-clock (s_memtime) and
+ * real-time (100 MHz) counter deltas over the read loop to clocks[2b] and clocks[2b+1] (device,
+ * 2*grid values, 16-byte aligned); bytes per clock per CU = iters * 16384 * waves / clocks[2b].
+ * sink: device, grid words, written only in the unlikely case that the data's checksum hits a
+ * constant (it keeps the reads from being optimised away).  1 <= grid <= 65536. */
+int dwdp_diag_lds_read(int grid, int waves, int iters, uint32_t* sink, unsigned long long* clocks,
+                       void* stream);
+
 /* Tile trace of the expert GEMM (bf16 and fp8 paths).  A library built with
  * -DDWDP_TILE_TRACE=1 has every workgroup of an expert-GEMM launch write one record into a fixed
  * device array of 131072 records, at the workgroup's index: its tile, the XCD it ran on and the

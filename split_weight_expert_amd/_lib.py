@@ -70,6 +70,7 @@ SIGNATURES = {
     "dwdp_quantize_weight_fp8": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "dwdp_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32]),
     "dwdp_diag_operand_stream": (_i32, [_vp, _sz, _sz, _i32, _i32, _i32, _i32, _vp]),
+    "dwdp_diag_lds_read": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp]),
     "dwdp_diag_tile_trace_clear": (_i32, [_vp]),
     "dwdp_diag_tile_trace_read": (_i32, [_vp, _sz, ctypes.POINTER(_sz)]),
     "dwdp_last_error": (ctypes.c_char_p, []),

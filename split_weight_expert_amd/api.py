@@ -197,6 +197,20 @@ def diag_operand_stream(src, span, stride, iters, grid, in_flight=3, cpol=0, str
                                                     _stream(stream)))
 
 
+def diag_lds_read(grid, waves, iters, stream=None):
+    """LDS read probe; returns (bytes per shader clock per CU, shader-clock GHz) averaged over the
+    workgroups (synchronises the stream)."""
+    import numpy as np
+    dev = torch.device("cuda", torch.cuda.current_device())
+    sink = torch.zeros(grid, dtype=torch.int32, device=dev)
+    clocks = torch.zeros(2 * grid, dtype=torch.int64, device=dev)
+    _lib.check(_lib.load().dwdp_diag_lds_read(grid, waves, iters, _ptr(sink), _ptr(clocks), _stream(stream)))
+    (stream or torch.cuda.current_stream()).synchronize()
+    c = clocks.cpu().numpy().astype(np.float64).reshape(grid, 2)
+    nbytes = float(iters) * 16384 * waves
+    return float(np.mean(nbytes / c[:, 0])), float(np.mean(c[:, 0] / (c[:, 1] * 10.0)))
+
+
 def diag_tile_trace_clear(stream=None):
     _lib.check(_lib.load().dwdp_diag_tile_trace_clear(_stream(stream)))
 

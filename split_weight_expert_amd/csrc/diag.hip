@@ -1,3 +1,5 @@
+// Diagnostics of the machine (not steps of the MoE block).
+//
 // Operand-stream probe: how fast workgroups move bytes from device memory into LDS with
 // global_load_lds, the path every operand of the expert GEMM takes (a diagnostic, not a step of the
 // MoE block).  Each workgroup has the GEMM's shape -- 512 threads, one per compute unit, a ring of
@@ -67,10 +69,60 @@ void launch_probe(int in_flight, dim3 grid, hipStream_t st, const uint8_t* src, 
     }
 }
 
+// LDS read probe: every wave reads 16-byte slots of a 128 KB LDS array with ds_read_b128, each lane a
+// consecutive slot (no bank conflicts), Q reads in flight between uses; thread 0 stores the workgroup's
+// shader-clock (s_memtime) and real-time (s_memrealtime, 100 MHz) deltas over the loop.
+constexpr int kLdsSlots = 8192;
+constexpr int kLdsQ = 16;
+
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void lds_read_kernel(int iters, uint32_t* __restrict__ sink,
+                                                           unsigned long long* __restrict__ clocks) {
+    __shared__ __attribute__((aligned(16))) uint4 buf[kLdsSlots];
+    for (int i = threadIdx.x; i < kLdsSlots; i += THREADS) buf[i] = uint4{(uint32_t)i, (uint32_t)i + 1u, 2u, 3u};
+    __syncthreads();
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint4 acc{0, 0, 0, 0};
+    const unsigned long long c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int q = 0; q < kLdsQ; ++q) {
+            const uint4 v = buf[((it * kLdsQ + q) * 64 + w * 1024 + lane) & (kLdsSlots - 1)];
+            acc.x ^= v.x;
+            acc.y ^= v.y;
+            acc.z ^= v.z;
+            acc.w ^= v.w;
+        }
+    }
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    // a store the compiler cannot drop, taken (almost) never: keeps the reads
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[blockIdx.x] = acc.x;
+    if (threadIdx.x == 0) {
+        clocks[2 * (size_t)blockIdx.x] = c1 - c0;
+        clocks[2 * (size_t)blockIdx.x + 1] = r1 - r0;
+    }
+}
+
 }  // namespace
 }  // namespace dwdp
 
 using namespace dwdp;
+
+extern "C" int dwdp_diag_lds_read(int grid, int waves, int iters, uint32_t* sink, unsigned long long* clocks,
+                                  void* stream) {
+    clear_error();
+    DWDP_REQUIRE(grid >= 1 && grid <= 65536, "grid must be in [1, 65536]");
+    DWDP_REQUIRE(waves == 4 || waves == 8 || waves == 16, "waves must be 4, 8 or 16");
+    DWDP_REQUIRE(iters >= 1, "iters must be at least 1");
+    DWDP_REQUIRE(sink != nullptr && clocks != nullptr, "null pointer argument");
+    DWDP_REQUIRE(aligned16(clocks), "clocks must be 16-byte aligned");
+    hipStream_t st = as_stream(stream);
+    if (waves == 4) hipLaunchKernelGGL(lds_read_kernel<256>, dim3(grid), dim3(256), 0, st, iters, sink, clocks);
+    else if (waves == 8) hipLaunchKernelGGL(lds_read_kernel<512>, dim3(grid), dim3(512), 0, st, iters, sink, clocks);
+    else hipLaunchKernelGGL(lds_read_kernel<1024>, dim3(grid), dim3(1024), 0, st, iters, sink, clocks);
+    DWDP_LAUNCHED();
+    return DWDP_OK;
+}
 
 extern "C" int dwdp_diag_operand_stream(const void* src, size_t span, size_t stride, int iters, int grid,
                                         int in_flight, int cpol, void* stream) {

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lib_mod.SIGNATURES), "binding signatures and header disagree"
@@ -229,6 +229,12 @@ def test_diagnostics_reject_bad_arguments_and_the_default_build_has_no_tile_trac
     expect(E_, f(FAKE, MiB, 0, 1, 1, 0, 0, None), lib, "in_flight")
     expect(E_, f(FAKE, MiB, 0, 1, 1, 6, 0, None), lib, "in_flight")
     expect(E_, f(FAKE, MiB, 0, 1, 1, 3, 1, None), lib, "cpol")
+    g = lib.dwdp_diag_lds_read
+    expect(E_, g(0, 8, 1, FAKE, FAKE, None), lib, "grid")
+    expect(E_, g(1, 6, 1, FAKE, FAKE, None), lib, "waves")
+    expect(E_, g(1, 8, 0, FAKE, FAKE, None), lib, "iters")
+    expect(E_, g(1, 8, 1, None, FAKE, None), lib, "null")
+    expect(E_, g(1, 8, 1, FAKE, ODD, None), lib, "aligned")
     assert ctypes.sizeof(lib_mod.TileRecord) == 48
     n = ctypes.c_size_t(7)
     buf = (lib_mod.TileRecord * 4)()

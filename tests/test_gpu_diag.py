@@ -38,6 +38,13 @@ def test_operand_stream_probe_runs_every_configuration():
         api.diag_operand_stream(buf, span, span, 1, grid + 1)        # would read past the tensor
 
 
+def test_lds_read_probe_reports_a_plausible_rate():
+    from split_weight_expert_amd import api
+    for waves in (4, 8, 16):
+        bpc, ghz = api.diag_lds_read(4, waves, 200)
+        assert 0.5 < ghz < 3.0 and 16 < bpc < 4096, (waves, bpc, ghz)
+
+
 def _problem(dt, counts, H, I, seed):
     from split_weight_expert_amd import ExpertStore, api
     from split_weight_expert_amd.moe import DTYPES
