@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--occupancy-probe", action="store_true",
                     help="time the block beside idle spinning workgroups (torch.cuda._sleep) that only occupy "
                          "compute units: 1, 4 and 16 of them for the block's length, and 1 for a quarter of it")
+    ap.add_argument("--mechanism-probe", action="store_true",
+                    help="time the block beside streams that isolate parts of the copy's cost: a read-only stream "
+                         "(the operand-stream probe over the source regions, 48 workgroups), a write-only stream (a "
+                         "fill of the pull's bytes), and the copy on compute units masked off from the block's")
     ap.add_argument("--copy-streams", type=int, default=1,
                     help="deal the prefetch's source regions round-robin over this many copy streams (the kernel "
                          "engine splits --copy-workgroups between them)")
@@ -500,6 +504,8 @@ def run_workload(cfg, args, steps, warmup, main):
         res["shape_study"] = measure_shapes(layer, block, cfg, b)
     if main and args.occupancy_probe:
         res["occupancy_probe"] = measure_occupancy(step, cfg)
+    if main and args.mechanism_probe and want_prefetch:
+        res["mechanism_probe"] = measure_mechanisms(layer, block, table, b, cfg)
     del layer, block, b, table
     torch.cuda.synchronize()
     return res
@@ -892,6 +898,147 @@ def measure_occupancy(step, cfg, reps=8):
         out["cases"].append(dict(workgroups=n, spin_ms=ms, block_ms=t, slowdown=t / alone - 1.0))
         log(f"{cfg.name}: block beside {n} idle workgroup(s) spinning {ms:.1f} ms: {alone:.3f} -> {t:.3f} ms "
             f"({t / alone - 1:+.1%})")
+    return out
+
+
+def _hip_runtime():
+    """The HIP runtime this process already uses (torch's), for calls that torch does not expose."""
+    import ctypes
+    path = [line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line][0]
+    return ctypes.CDLL(path)
+
+
+def cu_masked_stream(hip, mask_words):
+    """A stream whose kernels run only on the compute units set in mask_words (hipExtStreamCreateWithCUMask;
+    default priority)."""
+    import ctypes
+
+    import torch
+    arr = (ctypes.c_uint32 * len(mask_words))(*mask_words)
+    s = ctypes.c_void_p()
+    fn = hip.hipExtStreamCreateWithCUMask
+    fn.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32)]
+    rc = fn(ctypes.byref(s), len(mask_words), arr)
+    if rc != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask returned {rc}")
+    return torch.cuda.ExternalStream(s.value)
+
+
+def measure_mechanisms(layer, block, table, b, cfg, reps=8, copy_bits=8):
+    """The block (single-step protocol: an event, the block, an event, from an idle GPU; medians) beside
+    streams that each keep one property of the prefetch copy:
+      read_only   the operand-stream probe reading the three source regions, 16 workgroups each on three
+                  streams (48, the copy kernel's default), with non-temporal loads like the copy's and with
+                  loads that allocate in L2: its reads, no writes;
+      write_only  a fill of the pull's bytes in the other slot set: its writes, no reads;
+      cu_split    the copy kernel itself (3 workgroups per compute unit it may use) on a stream masked to
+                  copy_bits of every 32 compute units, and the block on a stream masked to the others, so
+                  that no compute unit holds both."""
+    import torch
+
+    from split_weight_expert_amd import api
+    x, wr, bias = layer.x, layer.w_router, layer.bias
+    comp = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    dst = layer.store.buffers[2]
+    pull = sum(n for _, _, n in layer.sources)
+
+    def block_on(s):
+        block.route(x, wr, bias, b, s)
+        block.permute(x, b, s)
+        block.ffn_stage(1, table, b, s)
+        block.ffn_stage(2, table, b, s)
+        block.combine(b, s)
+
+    def single(s, extra=None, side_streams=()):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        if extra is not None:
+            for ss in side_streams:
+                ss.wait_event(e0)
+            extra(side_streams)
+        block_on(s)
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def timed(fn, streams):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(streams[0])
+        for ss in streams[1:]:
+            ss.wait_event(e0)
+        fn(streams)
+        ends = []
+        for ss in streams:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(ss)
+            ends.append(e)
+        torch.cuda.synchronize()
+        return max(e0.elapsed_time(e) for e in ends)
+
+    med = lambda f: float(np.median([f() for _ in range(reps)]))
+    src_views = []
+    for ptr, _, n in layer.sources:
+        span = (n // 16) // 32768 * 32768
+        src_views.append((ptr, span))
+    src_tensors = {}
+    for buf in layer.src_store.buffers:
+        src_tensors[buf.data_ptr()] = buf
+
+    sides = [torch.cuda.Stream() for _ in src_views]
+
+    def read_only(cpol):
+        def go(streams):
+            for (ptr, span), ss in zip(src_views, streams):
+                api.diag_operand_stream(src_tensors[ptr], span, span, 1, 16, 3, cpol, ss)
+        return go
+
+    def write_only(streams):
+        with torch.cuda.stream(streams[0]):
+            dst[:pull].zero_()
+
+    out = dict(workload=cfg.name, reps=reps)
+    single(comp)
+    alone = med(lambda: single(comp))
+    out["block_ms_alone"] = alone
+    read_bytes = sum(sp * 16 for _, sp in src_views)
+    for name, fn, nbytes, ss in (("read_only_nontemporal", read_only(2), read_bytes, sides),
+                                 ("read_only_l2_allocating", read_only(0), read_bytes, sides),
+                                 ("write_only", write_only, pull, [side])):
+        fn(ss)
+        torch.cuda.synchronize()
+        t_side = med(lambda: timed(fn, ss))
+        t = med(lambda: single(comp, fn, ss))
+        out[name] = dict(bytes=nbytes, side_ms_alone=t_side, side_gbps=nbytes / t_side / 1e6, block_ms=t,
+                         slowdown=t / alone - 1.0)
+        log(f"{cfg.name}: block beside a {name.replace('_', '-')} stream ({nbytes / 1e9:.2f} GB, {t_side:.2f} ms alone): "
+            f"{alone:.3f} -> {t:.3f} ms ({t / alone - 1:+.1%})")
+    # compute units split between the block and the copy
+    hip = _hip_runtime()
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (ncu + 31) // 32
+    cmask = (1 << copy_bits) - 1
+    comp_m = cu_masked_stream(hip, [0xFFFFFFFF & ~cmask] * words)
+    copy_m = cu_masked_stream(hip, [cmask] * words)
+    n_copy_cu = copy_bits * words
+
+    def copy(streams):
+        api.prefetch_chunks(dst.data_ptr(), layer.sources, cfg.chunk_bytes, engine=api.COPY_KERNEL,
+                            max_workgroups=3 * n_copy_cu, copy_stream=streams[0])
+
+    single(comp_m)
+    masked_alone = med(lambda: single(comp_m))
+    copy([copy_m])
+    torch.cuda.synchronize()
+    copy_alone = med(lambda: timed(copy, [copy_m]))
+    beside = med(lambda: single(comp_m, copy, [copy_m]))
+    out["cu_split"] = dict(copy_cus=n_copy_cu, block_cus=ncu - n_copy_cu, copy_workgroups=3 * n_copy_cu,
+                           block_ms_alone_masked=masked_alone, copy_ms_alone_masked=copy_alone,
+                           block_ms_beside=beside, slowdown_vs_masked=beside / masked_alone - 1.0,
+                           slowdown_vs_all_cus=beside / alone - 1.0)
+    log(f"{cfg.name}: block on {ncu - n_copy_cu} CUs {masked_alone:.3f} ms alone ({masked_alone / alone - 1:+.1%} vs all "
+        f"CUs), {beside:.3f} ms beside the copy on the other {n_copy_cu} ({beside / masked_alone - 1:+.1%}); copy alone "
+        f"there {copy_alone:.2f} ms")
     return out
 
 
