@@ -224,11 +224,16 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool sorted = G <= kSortGroups;
     if (sorted && DWDP_SPARSE_ROWS == 0) {
+        // every thread compares its groups with all G: the row counts are read from LDS (one broadcast
+        // per h), not G times from global memory
+        __shared__ int rows_s[kSortGroups];
+        for (int g = tid; g < G; g += 1024) rows_s[g] = offsets[g + 1] - offsets[g];
+        __syncthreads();
         for (int g = tid; g < G; g += 1024) {
-            const int n = offsets[g + 1] - offsets[g];
+            const int n = rows_s[g];
             int rank = 0;
             for (int h = 0; h < G; ++h) {
-                const int m = offsets[h + 1] - offsets[h];
+                const int m = rows_s[h];
                 rank += (m > n) || (m == n && h < g);
             }
             order_s[rank] = g;
