@@ -159,6 +159,12 @@ const char* dwdp_version(void) {
 #ifdef DWDP_YPERM_NT
            " yperm-nt=" DWDP_STR(DWDP_YPERM_NT)
 #endif
+#ifdef DWDP_CLUSTER_GEMM1_LOG2
+           " cluster-gemm1-log2=" DWDP_STR(DWDP_CLUSTER_GEMM1_LOG2)
+#endif
+#ifdef DWDP_CLUSTER_GEMM2_LOG2
+           " cluster-gemm2-log2=" DWDP_STR(DWDP_CLUSTER_GEMM2_LOG2)
+#endif
 #ifdef DWDP_TICKET_TILES
            " ticket-tiles=" DWDP_STR(DWDP_TICKET_TILES)
 #endif
