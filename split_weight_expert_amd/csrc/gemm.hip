@@ -130,6 +130,9 @@ static_assert(DWDP_CLUSTER_GEMM1_LOG2 >= 0 && DWDP_CLUSTER_GEMM1_LOG2 <= 5 && DW
 #ifndef DWDP_MSUPER_FP8
 #define DWDP_MSUPER_FP8 4
 #endif
+#ifndef DWDP_MSUPER_FP8_GEMM2
+#define DWDP_MSUPER_FP8_GEMM2 8
+#endif
 #ifndef DWDP_MSUPER_BALANCED
 #define DWDP_MSUPER_BALANCED 0
 #endif
@@ -1494,6 +1497,9 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     p2.out = static_cast<uint8_t*>(y_perm);
     p2.out_scale = nullptr;
     p2.cluster_log2 = DWDP_CLUSTER_GEMM2_LOG2;
+    // fp8 GEMM2 takes super-blocks of 8 m-tiles (16K fp8 GEMM2 3.41-3.42 ms against 3.44-3.46 with 4;
+    // bf16 GEMM2 was not faster with 1, 2 or 8)
+    if (w_dtype == DWDP_FP8_E4M3) p2.msuper = DWDP_MSUPER_FP8_GEMM2;
     // 32-row tiles (a few rows per group, as in decode) share next to nothing: they draw tickets, so
     // that every XCD keeps taking tiles until none are left.  The schedule kernel zeroes both counters
     // (p2.ticket = p1.ticket + 1), and each launch's last draw resets its own.

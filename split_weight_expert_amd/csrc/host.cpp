@@ -141,6 +141,9 @@ const char* dwdp_version(void) {
 #ifdef DWDP_MSUPER_FP8
            " msuper-fp8=" DWDP_STR(DWDP_MSUPER_FP8)
 #endif
+#ifdef DWDP_MSUPER_FP8_GEMM2
+           " msuper-fp8-gemm2=" DWDP_STR(DWDP_MSUPER_FP8_GEMM2)
+#endif
 #ifdef DWDP_MSUPER_BALANCED
            " msuper-balanced=" DWDP_STR(DWDP_MSUPER_BALANCED)
 #endif
