@@ -85,7 +85,6 @@ struct GemmParams {
     float* out_scale;               // GEMM1 fp8: A scales [rows, I/128]
     int32_t* ticket;                // expert GEMMs: tile ticket counter (tiles drawn in schedule order), or
                                     // null (tile fixed by the workgroup index, clusters dealt over the XCDs)
-    int cluster_log2;               // expert GEMMs: log2 of the tiles per dealt cluster
 };
 
 struct Tile {
@@ -1114,7 +1113,7 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
         lin = *s_ticket;
         __syncthreads();
     } else {
-        lin = dealt_lin(p.cluster_log2);
+        lin = dealt_lin(KIND == kGemm1 ? DWDP_CLUSTER_GEMM1_LOG2 : DWDP_CLUSTER_GEMM2_LOG2);
     }
     if (!decode_tile<BM, KIND>(p, c.t, lin)) return;
 #if DWDP_TILE_TRACE
@@ -1481,7 +1480,6 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     p1.I = I;
     p1.NT = w_dtype == DWDP_F32 ? I / (kBnF32 / 2) : I / (kBnDma / 2);
     p1.msuper = w_dtype == DWDP_FP8_E4M3 ? DWDP_MSUPER_FP8 : DWDP_MSUPER_BF16;
-    p1.cluster_log2 = DWDP_CLUSTER_GEMM1_LOG2;
     p1.out = base + L.a;
     p1.out_scale = reinterpret_cast<float*>(base + L.a_scale);
 
@@ -1496,7 +1494,6 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
     p2.NT = w_dtype == DWDP_F32 ? H / kBnF32 : H / kBnDma;
     p2.out = static_cast<uint8_t*>(y_perm);
     p2.out_scale = nullptr;
-    p2.cluster_log2 = DWDP_CLUSTER_GEMM2_LOG2;
     // fp8 GEMM2 takes super-blocks of 8 m-tiles (16K fp8 GEMM2 3.41-3.42 ms against 3.44-3.46 with 4;
     // bf16 GEMM2 was not faster with 1, 2 or 8)
     if (w_dtype == DWDP_FP8_E4M3) p2.msuper = DWDP_MSUPER_FP8_GEMM2;
