@@ -130,3 +130,99 @@ def test_tile_trace_covers_every_tile_once_and_changes_no_result(dt, mode):
                 assert (cov == 1).all(), f"stage {stage} group {g} n-tile {nt}: rows covered {np.unique(cov)}"
             assert set(mine["n_tile"].tolist()) == set(range(n_tiles))
             assert (mine["group_m_tiles"] == len(np.unique(mine["first_row"]))).all()
+
+
+def _coverage(tr, counts, n_tiles):
+    """Every (group, n-tile) of the schedule ran: its tiles' rows cover the group's rows exactly once."""
+    off = np.concatenate([[0], np.cumsum(counts)])
+    assert len(np.unique(tr["order"])) == len(tr), "a schedule position ran twice"
+    seen = np.zeros((len(counts), n_tiles), np.int64)
+    for g in np.unique(tr["group"]):
+        mine = tr[tr["group"] == g]
+        for nt in range(n_tiles):
+            sel = mine[mine["n_tile"] == nt]
+            cov = np.zeros(counts[g], np.int32)
+            for r in sel:
+                lo = r["first_row"] - off[g]
+                assert 0 <= lo and lo + r["rows"] <= counts[g] and r["rows"] > 0
+                cov[lo:lo + r["rows"]] += 1
+            assert (cov == 1).all(), f"group {g} n-tile {nt}: rows covered {np.unique(cov)}"
+            seen[g, nt] = len(sel)
+        assert (mine["group_m_tiles"] == len(np.unique(mine["first_row"]))).all()
+    assert (tr["t_end"] >= tr["t_start"]).all()
+    assert ((seen > 0) == (np.asarray(counts)[:, None] > 0)).all(), "a non-empty group missed an n-tile"
+
+
+# Full-size tile schedules (H = 7168, I = 2048, 256 routed experts + 1 shared): every group's table entry
+# points at one shared expert record, so only the row counts -- all the schedule depends on -- are real.
+FULL_COUNTS = {
+    # 8K bf16-like: skewed counts summing to 65536 routed rows, some empty, + 8192 shared rows
+    "prefill8k_bf16": ("bf16", 11),
+    # 16K fp8-like: near-balanced counts (131072 routed rows) + 16384 shared
+    "prefill16k_fp8": ("fp8", 12),
+    # decode-like: 512 routed rows over 256 experts (32-row ticket tiles) + 64 shared
+    "decode64_bf16": ("bf16", 13),
+}
+
+
+def _full_counts(name, seed):
+    rng = np.random.default_rng(seed)
+    E = 256
+    if name == "prefill8k_bf16":
+        w = rng.pareto(1.2, E) + 0.02
+        w[rng.choice(E, 9, replace=False)] = 0
+        counts = rng.multinomial(65536, w / w.sum())
+        return np.concatenate([counts, [8192]])
+    if name == "prefill16k_fp8":
+        counts = rng.multinomial(131072, np.full(E, 1.0 / E))
+        return np.concatenate([counts, [16384]])
+    counts = rng.multinomial(512, np.full(E, 1.0 / E))
+    return np.concatenate([counts, [64]])
+
+
+@pytest.mark.parametrize("name", list(FULL_COUNTS))
+def test_tile_trace_full_size_schedules_cover_every_tile_once(name):
+    if not os.path.exists(TRACE_LIB):
+        pytest.skip("no tile-trace build")
+    from split_weight_expert_amd import ExpertStore, _lib, api
+    from split_weight_expert_amd.moe import DTYPES
+    dt, seed = FULL_COUNTS[name]
+    H, I = 7168, 2048
+    counts = _full_counts(name, seed)
+    G, rows = len(counts), int(counts.sum())
+    print(f"{name}: {G} groups, {rows} rows", flush=True)
+    rng = np.random.default_rng(seed)
+    store = ExpertStore(H, I, DTYPES[dt], [1], device=DEV)
+    store.load(0, 0, *[torch.from_numpy(rng.standard_normal(s).astype(np.float32) / np.sqrt(s[1])).to(DEV)
+                       for s in ((I, H), (I, H), (H, I))])
+    table = store.table([(0, 0)] * G, DEV)
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(DEV)
+    x = torch.randn(rows, H, device=DEV).to(torch.bfloat16)
+    if dt == "fp8":
+        xq = torch.empty(rows, H, dtype=torch.uint8, device=DEV)
+        xs = torch.empty(rows, H // 128, dtype=torch.float32, device=DEV)
+        api.quantize_tokens_fp8(x, xq, xs)
+        x, x_scale, wcode = xq, xs, api.FP8_E4M3
+    else:
+        x_scale, wcode = None, api.BF16
+    ws = torch.empty(api.workspace_bytes(api.OP_GROUPED_FFN, rows, 1, G, H, I, wcode, 0), dtype=torch.uint8,
+                     device=DEV)
+    y = torch.empty(rows, H, dtype=torch.bfloat16, device=DEV)
+    saved = _lib._lib
+    _lib._lib = None
+    try:
+        _lib.load(TRACE_LIB)
+        traces = {}
+        for stage in (1, 2):
+            api.diag_tile_trace_clear()
+            api.moe_grouped_ffn_stage(stage, table, G, offsets, x, x_scale, H, I, wcode, y, ws)
+            torch.cuda.synchronize()
+            tr = api.diag_tile_trace_read()
+            traces[stage] = tr[tr["t_end"] > 0]
+    finally:
+        _lib._lib = saved
+    for stage, n_tiles in ((1, I // 128), (2, H // 256)):
+        _coverage(traces[stage], counts, n_tiles)
+        assert ((traces[stage]["xcd"] >= 0) & (traces[stage]["xcd"] < 8)).all()
+    del store, table, x, ws, y
+    torch.cuda.empty_cache()
