@@ -15,14 +15,16 @@
 //     slab run together on one XCD's L2.
 //   * bf16 / fp8 (gemm_frag_kernel): weights are stored fragment-major, every
 //     operand goes global -> LDS by DMA into a multi-stage ring, and the
-//     MFMAs are v_mfma_f32_32x32x16_bf16 or v_mfma_scale_f32_32x32x64_f8f6f4
-//     (unit scales, with a per-128-K fold of the fp32 block scales).  GEMM1's
+//     MFMAs are v_mfma_f32_32x32x16_bf16 or the unscaled fp8 form of
+//     v_mfma_f32_32x32x64_f8f6f4 (with a per-128-K fold of the fp32 block
+//     scales).  GEMM1's
 //     tile holds the gate and up rows of the same output columns, so SwiGLU
 //     (and for fp8 the re-quantisation of A) happens in the epilogue.
 //     GEMM1 reads its activation rows either from the permuted rows or from
 //     the token rows through perm_src.
 //   * f32 (small shapes only): LDS-tiled FMA kernel with the same schedule.
-//   * Router (bf16): router_mfma_kernel, a plain two-stage MFMA tile kernel.
+//   * Router (bf16): router_dma_kernel (up to 512 tiles: operands by DMA into
+//     a four-slot LDS ring) or router_mfma_kernel (two-stage, register-staged).
 #include <algorithm>
 #include <mutex>
 
@@ -37,6 +39,16 @@
 // build compiles none of it.
 #ifndef DWDP_TILE_TRACE
 #define DWDP_TILE_TRACE 0
+#endif
+// E8M0 block-scale code passed to the fp8 MFMA builtin.  The block scales of this path are fp32 and are
+// applied in the fold, so the MFMA itself must not scale: with code 0 the compiler emits the unscaled
+// v_mfma_f32_32x32x64_f8f6f4 (8 bytes shorter than the scaled form; 16K fp8 block 0.5% faster), with 127
+// (2^0) the scaled form with unit scales.  Both give the same products.
+#ifndef DWDP_ROUTER_DMA
+#define DWDP_ROUTER_DMA 1
+#endif
+#ifndef DWDP_MFMA_E8M0
+#define DWDP_MFMA_E8M0 0
 #endif
 
 namespace dwdp {
@@ -586,6 +598,88 @@ __device__ __forceinline__ int aslot(int row, int chunk) {
     return ROWB == 128 ? chunk ^ ((row >> 1) & 7) : chunk ^ ((row >> 2) & 3);
 }
 
+// Router (bf16) with its operands moved by DMA: the router_mfma_kernel tile (64 x 64, 4 waves of 32 x 32,
+// K steps of 64 columns) with global_load_lds into an NS-slot LDS ring and P = NS - 1 steps in flight,
+// so a workgroup keeps three 16 KB steps of loads outstanding without staging them in registers.  Wave w
+// fills the 1 KB blocks 2w and 2w+1 of the step's A rows and of its B rows: lane l of block b carries
+// row 8b + l/8 into LDS slot l % 8, which holds that row's 16-byte chunk aslot(row, l % 8).  Slot
+// (kt + P) % NS is the one step kt - 1 read, so step kt + P is issued after step kt's barrier.
+template <int NS>
+__global__ __launch_bounds__(256) void router_dma_kernel(GemmParams p) {
+    constexpr int BM = 64, BN = 64, ROWB = 128, ABYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
+    constexpr int P = NS - 1;
+    static_assert(NS >= 2 && NS <= 4, "ring depth (the waits below cover up to 3 steps in flight)");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE];
+
+    Tile t;
+    if (!decode_tile<BM, kRouter>(p, t)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, hi = lane >> 5;
+    const size_t ldk = (size_t)p.K * 2;
+    const int KT = p.K / 64;
+
+    const uint8_t* ga[2];
+    const uint8_t* gb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = (2 * wave + q) * 8 + lane / 8;
+        const int c = aslot<ROWB>(r, lane & 7);
+        ga[q] = p.a + (size_t)(t.row0 + min(r, t.nrows - 1)) * ldk + c * 16;
+        gb[q] = p.b_single + (size_t)min(t.nt * BN + r, p.N - 1) * ldk + c * 16;
+    }
+    auto issue = [&](int kt) {
+        uint8_t* st = ring + (kt % NS) * STAGE;
+        const size_t off = (size_t)kt * ROWB;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) dma16(ga[q] + off, st + (2 * wave + q) * 1024);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) dma16(gb[q] + off, st + ABYTES + (2 * wave + q) * 1024);
+    };
+    auto frag = [&](const uint8_t* S, int row, int chunk) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(S + row * ROWB + (aslot<ROWB>(row, chunk) << 4)));
+    };
+
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    const bool active = wm * 32 < t.nrows;
+    for (int k = 0; k < P && k < KT; ++k) issue(k);
+    for (int kt = 0; kt < KT; ++kt) {
+        // this wave's DMAs of step kt have landed once at most those of the later issued steps are out
+        const int later = min(P - 1, KT - 1 - kt);
+        if (later >= 2) wait_vmcnt<8>();
+        else if (later == 1) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
+        ordered_barrier();                     // every wave's step kt landed; step kt-1's slot is free
+        if (kt + P < KT) issue(kt + P);
+        const uint8_t* A = ring + (kt % NS) * STAGE;
+        const uint8_t* B = A + ABYTES;
+        if (active) {
+            bf16x8 af[4], bf[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                af[s] = frag(A, wm * 32 + l32, 2 * s + hi);
+                bf[s] = frag(B, wn * 32 + l32, 2 * s + hi);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], bf[s], acc, 0, 0, 0);
+        }
+        // the fragments are in registers before any wave passes the next barrier
+        __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0), vmcnt and expcnt not waited on
+    }
+
+    float* out = reinterpret_cast<float*>(p.out);
+    const int col = t.nt * BN + wn * 32 + l32;
+    if (col < p.N) {
+        const float b = p.bias ? p.bias[col] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = wm * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            if (m < t.nrows) out[(size_t)(t.row0 + m) * p.N + col] = acc[r] + b;
+        }
+    }
+}
+
 // Main loop and epilogue of one tile with MA active 32-row m-blocks, of which this wave multiplies
 // MWV (compile-time: the loop body is straight-line code; only the LDS ring is waited on, and only
 // here, with vmcnt).  Every wave loads its share of the MA blocks' rows whatever its MWV, and a wave
@@ -671,9 +765,9 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
     auto b_frag = [&](const uint8_t* B, int j, int v) -> u32x4 {
         return *reinterpret_cast<const u32x4*>(B + (cg * BI + j * BF + v) * 1024 + lane * 16);
     };
-    // fp8 step: per m-block, the two 64-wide halves of the 128-wide K block go through the scaled
-    // MFMA (unit scales) into a fresh partial sum, which is folded into the accumulator with the
-    // row scale times the weight block's scale.
+    // fp8 step: per m-block, the two 64-wide halves of the 128-wide K block go through the unscaled
+    // fp8 MFMA into a fresh partial sum, which is folded into the accumulator with the row scale
+    // times the weight block's scale.
     // fp8 step kt; the DMA of step ikt into slot ibuf (when iss) is spread over its MFMA blocks, so a
     // wave never waits for the memory pipe to accept its whole batch before its first MFMA
     // fp8 with 64-byte K steps (256-row tiles): the accumulator is kept in units of the current K block's
@@ -733,8 +827,8 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
             };
             auto mfma = [&](int b) {
                 const int i = b / NJ, j = b % NJ;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0, 127,
-                                                                            0, 127);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0,
+                                                                            DWDP_MFMA_E8M0, 0, DWDP_MFMA_E8M0);
             };
             if (first) {
                 // block b's rescale runs under block b-1's MFMA
@@ -808,7 +902,8 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
 #pragma unroll
                 for (int s = 0; s < SH; ++s)
                     part[b & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j][s], af[i][s], part[b & 1], 0, 0,
-                                                                                  0, 127, 0, 127);
+                                                                                  0, DWDP_MFMA_E8M0, 0,
+                                                                                  DWDP_MFMA_E8M0);
             };
             constexpr int NB = MW * NJ, QB = (PER + NB - 1) / NB;   // DMA instructions per block
             constexpr int NF = 17;                                  // VALU per fold
@@ -1324,7 +1419,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // Expert GEMMs (bf16, fp8): gemm_frag_kernel, BM x 256 tiles with BM = 32, 64, 128 or 256 (fp8: at
 // most 128) picked from the mean rows per group (decode batches give groups of a few rows).
 // f32: 64 x 64 FMA tiles.
-// Router (bf16): router_mfma_kernel, 64 x 64 tiles.
+// Router (bf16): router_dma_kernel or router_mfma_kernel, 64 x 64 tiles.
 constexpr int kBnDma = 256;
 constexpr int kBmF32 = 64, kBnF32 = 64;
 constexpr int kBmRouter = 64, kBnRouter = 64;
@@ -1357,8 +1452,16 @@ int64_t xcd_grid(int64_t tiles) {
 
 template <int BM, int BN, int WM, int WN>
 void launch_router(const GemmParams& p, int64_t tiles, hipStream_t st) {
-    hipLaunchKernelGGL((router_mfma_kernel<BM, BN, WM, WN>), dim3((unsigned)xcd_grid(tiles)), dim3(WM * WN * 64), 0,
-                       st, p);
+    static_assert(BM == 64 && BN == 64 && WM == 2 && WN == 2, "the DMA router has one tile shape");
+    // Up to two tiles per compute unit the DMA form is faster (its 64 KB ring leaves room for two
+    // workgroups per unit, each with three steps in flight); larger batches need more workgroups per unit
+    // at once, which the register-staged kernel's 32 KB allow.
+    if (DWDP_ROUTER_DMA && tiles <= 2 * 256) {
+        hipLaunchKernelGGL(router_dma_kernel<4>, dim3((unsigned)xcd_grid(tiles)), dim3(256), 0, st, p);
+    } else {
+        hipLaunchKernelGGL((router_mfma_kernel<BM, BN, WM, WN>), dim3((unsigned)xcd_grid(tiles)), dim3(WM * WN * 64),
+                           0, st, p);
+    }
 }
 
 template <int KIND>

@@ -174,6 +174,15 @@ const char* dwdp_version(void) {
 #ifdef DWDP_TILE_TRACE
            " tile-trace=" DWDP_STR(DWDP_TILE_TRACE)
 #endif
+#ifdef DWDP_MFMA_E8M0
+           " mfma-e8m0=" DWDP_STR(DWDP_MFMA_E8M0)
+#endif
+#ifdef DWDP_ROUTER_DMA
+           " router-dma=" DWDP_STR(DWDP_ROUTER_DMA)
+#endif
+#ifdef DWDP_ROUTER_SPLITK_TILE
+           " router-splitk-tile=" DWDP_STR(DWDP_ROUTER_SPLITK_TILE)
+#endif
 #ifdef DWDP_COMBINE_NT
            " combine-nt=" DWDP_STR(DWDP_COMBINE_NT)
 #endif

@@ -2,11 +2,13 @@
 // renormalised softmax weights.  The pages give no gate formula; the gate here is
 // softmax top-k with the weights renormalised over the chosen k.
 //
-// Logits: prefill batches use the tiled MFMA kernel of gemm.hip.  A decode-sized
-// batch (T <= 256 tokens, bf16) would give that kernel only a few workgroups, each
-// walking all of K, so it uses router_splitk_kernel here: 32 x 32 tiles, the K range
-// split over the workgroup's 8 waves, partial tiles summed through LDS in wave order
-// (a fixed order, so the logits are reproducible bit for bit).
+// Logits: prefill batches use the tiled MFMA kernels of gemm.hip.  A decode-sized
+// batch (T <= 256 tokens, bf16) would give those only a few workgroups, each
+// walking all of K, so it uses a split-K kernel here: 16 x 16 tiles with the K range
+// split over the workgroup's 16 waves (router_splitk16_kernel; the 32 x 32 form with
+// 8 waves, router_splitk_kernel, is the build option DWDP_ROUTER_SPLITK_TILE=32 and
+// took the 64-token route stage 47 us against 29 us), partial tiles summed through
+// LDS in wave order (a fixed order, so the logits are reproducible bit for bit).
 //
 // Top-k: one wavefront per token.  Lane l holds logits l, l+64, l+128, ...;
 // k rounds of (lane-local best, then a 64-lane butterfly max on (value desc,
@@ -80,6 +82,62 @@ __global__ __launch_bounds__(kSplitWaves * 64) void router_splitk_kernel(const u
         }
     }
 }
+
+// The same with 16 x 16 tiles (v_mfma_f32_16x16x32_bf16) and the K range split over 16 waves: four
+// times the workgroups of the 32 x 32 form, so a 64-token batch spreads its loads over 64 compute
+// units instead of 16, and each wave walks H/16 columns in batches of 8 K steps.  Wave w takes the
+// 32-column K steps [w S / 16, (w+1) S / 16) of the S = H / 32 (any H % 32 == 0).  Operand lanes:
+// row (or expert) l % 16, 8 columns at 8 (l / 16) of the step; result element r of lane l: token
+// m0 + 4 (l / 16) + r, expert n0 + l % 16.  Partials are summed through LDS in wave order.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kSplit16Waves = 16;
+
+__global__ __launch_bounds__(kSplit16Waves * 64) void router_splitk16_kernel(const uint16_t* __restrict__ x,
+                                                                            const uint16_t* __restrict__ wr,
+                                                                            const float* __restrict__ bias, int T,
+                                                                            int H, int E,
+                                                                            float* __restrict__ logits) {
+    __shared__ float part[kSplit16Waves][64][5];   // 5: consecutive lanes fall on different banks
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, q = lane >> 4;
+    const int m0 = blockIdx.x * 16, n0 = blockIdx.y * 16;
+    const uint16_t* arow = x + (size_t)min(m0 + l16, T - 1) * H + q * 8;
+    const uint16_t* brow = wr + (size_t)min(n0 + l16, E - 1) * H + q * 8;
+    const int steps = H / 32;
+    const int sb = wave * steps / kSplit16Waves, se = (wave + 1) * steps / kSplit16Waves;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int U = 8;                           // K steps per batch of loads
+    for (int s0 = sb; s0 < se; s0 += U) {
+        bf16x8 a[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u < se) {
+                a[u] = *reinterpret_cast<const bf16x8*>(arow + (s0 + u) * 32);
+                b[u] = *reinterpret_cast<const bf16x8*>(brow + (s0 + u) * 32);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (s0 + u < se) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave][lane][r] = acc[r];
+    __syncthreads();
+    if (wave == 0) {
+        const int e = n0 + l16;
+        const float b = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float s = part[0][lane][r];
+            for (int w = 1; w < kSplit16Waves; ++w) s += part[w][lane][r];
+            const int t = m0 + q * 4 + r;
+            if (t < T && e < E) logits[(size_t)t * E + e] = s + b;
+        }
+    }
+}
+
+#ifndef DWDP_ROUTER_SPLITK_TILE
+#define DWDP_ROUTER_SPLITK_TILE 16
+#endif
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
@@ -164,7 +222,12 @@ extern "C" int dwdp_route_topk(const void* x, const void* w_router, int in_dtype
     DWDP_REQUIRE(x && w_router && logits_out && topk_idx && topk_w, "null pointer argument");
     DWDP_REQUIRE(aligned16(x) && aligned16(w_router), "x and w_router must be 16-byte aligned");
     hipStream_t st = as_stream(stream);
-    if (in_dtype == DWDP_BF16 && T <= kSplitMaxT && H % (kSplitWaves * 16) == 0) {
+    if (DWDP_ROUTER_SPLITK_TILE == 16 && in_dtype == DWDP_BF16 && T <= kSplitMaxT) {
+        hipLaunchKernelGGL(router_splitk16_kernel, dim3((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16)),
+                           dim3(kSplit16Waves * 64), 0, st, static_cast<const uint16_t*>(x),
+                           static_cast<const uint16_t*>(w_router), bias, (int)T, H, E, logits_out);
+        DWDP_LAUNCHED();
+    } else if (in_dtype == DWDP_BF16 && T <= kSplitMaxT && H % (kSplitWaves * 16) == 0) {
         hipLaunchKernelGGL(router_splitk_kernel, dim3((unsigned)((T + 31) / 32), (unsigned)((E + 31) / 32)),
                            dim3(kSplitWaves * 64), 0, st, static_cast<const uint16_t*>(x),
                            static_cast<const uint16_t*>(w_router), bias, (int)T, H, E, logits_out);
