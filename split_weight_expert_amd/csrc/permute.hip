@@ -336,8 +336,10 @@ __global__ __launch_bounds__(256) void shared_rows_kernel(int32_t* __restrict__ 
     if (t < T) perm_src[R + t] = (int32_t)t;
 }
 
-// fp8 gather: 16 lanes per 128-column group, 8 bf16 values (16 bytes) per lane.  perm_src == NULL
-// quantises x row by row (output row r = token r).
+// fp8 gather: 16 lanes per 128-column group, 8 bf16 values (16 bytes) per lane; the 16 lane groups of
+// the workgroup take the row's column groups in batches of 4 each (all 4 loads issued before the first
+// is used, so a 7168-wide row costs one memory round trip, not four).  perm_src == NULL quantises x row
+// by row (output row r = token r).
 __global__ __launch_bounds__(256) void gather_fp8_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t R,
                                                          int64_t rows, int H, int32_t* __restrict__ perm_src,
                                                          uint8_t* __restrict__ q, float* __restrict__ qs) {
@@ -352,33 +354,40 @@ __global__ __launch_bounds__(256) void gather_fp8_kernel(const uint16_t* __restr
         const bool ok = src >= 0 && src < T;
         const int G = H / kFp8Group;
         const int sub = threadIdx.x & 15;
-        for (int g = threadIdx.x >> 4; g < G; g += 16) {
-            float v[8];
-            if (ok) {
-                const uint4 raw = *reinterpret_cast<const uint4*>(x + src * H + g * kFp8Group + sub * 8);
-                const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+        constexpr int U = 4;
+        for (int g0 = threadIdx.x >> 4; g0 < G; g0 += 16 * U) {
+            uint4 raw[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int g = g0 + 16 * u;
+                raw[u] = (ok && g < G) ? *reinterpret_cast<const uint4*>(x + src * H + g * kFp8Group + sub * 8)
+                                       : uint4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int g = g0 + 16 * u;
+                if (g >= G) break;                 // the same for all 16 lanes of the group
+                float v[8];
+                const uint32_t wds[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     v[2 * i] = bf16_to_f32((uint16_t)(wds[i] & 0xffffu));
                     v[2 * i + 1] = bf16_to_f32((uint16_t)(wds[i] >> 16));
                 }
-            } else {
+                float m = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+                for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+                for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
+                const float s = m == 0.0f ? 1.0f : m / 448.0f;
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lo |= (uint32_t)f32_to_e4m3(v[i] / s) << (8 * i);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hi |= (uint32_t)f32_to_e4m3(v[4 + i] / s) << (8 * i);
+                *reinterpret_cast<uint2*>(q + r * H + g * kFp8Group + sub * 8) = uint2{lo, hi};
+                if (sub == 0) qs[r * G + g] = s;
             }
-            float m = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-#pragma unroll
-            for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
-            const float s = m == 0.0f ? 1.0f : m / 448.0f;
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lo |= (uint32_t)f32_to_e4m3(v[i] / s) << (8 * i);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hi |= (uint32_t)f32_to_e4m3(v[4 + i] / s) << (8 * i);
-            *reinterpret_cast<uint2*>(q + r * H + g * kFp8Group + sub * 8) = uint2{lo, hi};
-            if (sub == 0) qs[r * G + g] = s;
         }
     }
 }

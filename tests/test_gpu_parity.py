@@ -574,9 +574,10 @@ def test_token_rows_equal_permuted_rows(dt):
         assert torch.equal(out[True][key], out[False][key]), key
 
 
-def test_token_quantiser_is_bit_exact():
+@pytest.mark.parametrize("H", [1024, 7168, 8960])   # 8, 56 and 70 groups: one and two batches of loads
+def test_token_quantiser_is_bit_exact(H):
     from split_weight_expert_amd import api
-    cfg = shrink(synth.get_config("prefill16k_fp8"), T=300, H=1024)
+    cfg = shrink(synth.get_config("prefill16k_fp8"), T=300, H=H)
     x = synth.tokens(cfg)
     x[5] = 0.0                                    # an all-zero token: scale 1
     xt = torch.from_numpy(x).to(DEV, torch.bfloat16)
