@@ -1127,9 +1127,8 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                     const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        uint32_t w = 0;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) w |= (uint32_t)f32_to_e4m3(av[i][4 * q + e] / sc) << (8 * e);
+                        const uint32_t w = e4m3x4(av[i][4 * q] / sc, av[i][4 * q + 1] / sc, av[i][4 * q + 2] / sc,
+                                                  av[i][4 * q + 3] / sc);
                         const int byte = cg * 32 + q * 8 + hi * 4;
                         *reinterpret_cast<uint32_t*>(codes + m * 128 + (((byte >> 4) ^ (m & 7)) << 4) + (byte & 15)) = w;
                     }

@@ -380,11 +380,8 @@ __global__ __launch_bounds__(256) void gather_fp8_kernel(const uint16_t* __restr
 #pragma unroll
                 for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
                 const float s = m == 0.0f ? 1.0f : m / 448.0f;
-                uint32_t lo = 0, hi = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) lo |= (uint32_t)f32_to_e4m3(v[i] / s) << (8 * i);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) hi |= (uint32_t)f32_to_e4m3(v[4 + i] / s) << (8 * i);
+                const uint32_t lo = e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+                const uint32_t hi = e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
                 *reinterpret_cast<uint2*>(q + r * H + g * kFp8Group + sub * 8) = uint2{lo, hi};
                 if (sub == 0) qs[r * G + g] = s;
             }

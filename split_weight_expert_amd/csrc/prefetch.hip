@@ -127,10 +127,8 @@ __global__ __launch_bounds__(256) void quantize_block_kernel(const float* __rest
     uint8_t* out = q + (br * kFp8Group + r) * cols + bc * kFp8Group + h * 64;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        uint32_t pk = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) pk |= (uint32_t)f32_to_e4m3(v[4 * i + b] / sc) << (8 * b);
-        reinterpret_cast<uint32_t*>(out)[i] = pk;
+        reinterpret_cast<uint32_t*>(out)[i] =
+            e4m3x4(v[4 * i] / sc, v[4 * i + 1] / sc, v[4 * i + 2] / sc, v[4 * i + 3] / sc);
     }
     if (t == 0) s[br * (cols / kFp8Group) + bc] = sc;
 }
