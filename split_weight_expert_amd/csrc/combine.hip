@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict_
                 uint32_t o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    o[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+                    o[i] = bf16x2(acc[2 * i], acc[2 * i + 1]);
                 *reinterpret_cast<uint4*>(y + (t * H + c * 8) * 2) = uint4{o[0], o[1], o[2], o[3]};
             } else {
                 float4* out = reinterpret_cast<float4*>(y + (t * H + c * 8) * 4);

@@ -30,12 +30,12 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 // ------------------------------------------------------------ device: numbers
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// Two fp32 values -> bf16 bits packed little-endian (a in the low half), round to nearest even, NaN
+// stays a quiet NaN: one hardware v_cvt_pk_bf16_f32.
+typedef float dwdp_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 dwdp_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((dwdp_f32x2){a, b}, dwdp_bf16x2));
 }
 
 // Four fp32 values -> OCP E4M3 codes (round to nearest even, subnormals kept), packed little-endian

@@ -177,6 +177,9 @@ const char* dwdp_version(void) {
 #ifdef DWDP_MFMA_E8M0
            " mfma-e8m0=" DWDP_STR(DWDP_MFMA_E8M0)
 #endif
+#ifdef DWDP_SILU_RCP
+           " silu-rcp=" DWDP_STR(DWDP_SILU_RCP)
+#endif
 #ifdef DWDP_ROUTER_DMA
            " router-dma=" DWDP_STR(DWDP_ROUTER_DMA)
 #endif
