@@ -1136,10 +1136,14 @@ __device__ __forceinline__ void frag_tile(const GemmParams& p, const TileCtx& c,
                     const int m = rbase + i * 32 + l32;
                     const float amax = fmaxf(fmaxf(red[m], red[BM + m]), fmaxf(red[2 * BM + m], red[3 * BM + m]));
                     const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+                    // A / scale as A * (1 / scale): one division a row instead of one a value (16K fp8
+                    // GEMM1 1.2% faster).  The product is within an ulp of the quotient, far inside the
+                    // window in which A's fp32 accumulation order already moves codes.
+                    const float rs = 1.0f / sc;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const uint32_t w = e4m3x4(av[i][4 * q] / sc, av[i][4 * q + 1] / sc, av[i][4 * q + 2] / sc,
-                                                  av[i][4 * q + 3] / sc);
+                        const uint32_t w = e4m3x4(av[i][4 * q] * rs, av[i][4 * q + 1] * rs, av[i][4 * q + 2] * rs,
+                                                  av[i][4 * q + 3] * rs);
                         const int byte = cg * 32 + q * 8 + hi * 4;
                         *reinterpret_cast<uint32_t*>(codes + m * 128 + (((byte >> 4) ^ (m & 7)) << 4) + (byte & 15)) = w;
                     }
