@@ -1,7 +1,7 @@
 // Weighted unpermute: y[t] = sum_j w[t,j] * y_perm[inv_perm[t,j]] (+ y_perm[T*k + t]),
 // summed in fp32 in slot order, then the shared row, rounded once.  One
 // workgroup per token (a bounded grid walks the tokens); each thread owns 8 consecutive columns (16-byte bf16
-// vectors) and issues the loads of up to 8 source rows together before summing
+// vectors) and issues the loads of up to 16 source rows together before summing
 // them in slot order.  Entries with inv_perm < 0 (dropped assignments) contribute
 // nothing.
 #include <algorithm>
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict_
         const int64_t shared_row = T * k + t;
         const int nvec = H / 8;
         const int nsrc = k + (shared ? 1 : 0);                // source rows: the k slots, then the shared row
-        constexpr int B = 8;                                  // rows whose loads are in flight together
+        constexpr int B = 16;                                 // rows whose loads are in flight together
         for (int c = threadIdx.x; c < nvec; c += 256) {
             float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
             for (int j0 = 0; j0 < nsrc; j0 += B) {

@@ -141,14 +141,16 @@ __global__ __launch_bounds__(kSplit16Waves * 64) void router_splitk16_kernel(con
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
-constexpr int kPerLane = kMaxE / 64;
 
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
+// PL logits per lane (E <= 64 PL): the per-lane scan of every round walks only the slots E needs.
+template <int PL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
                                                    int32_t* __restrict__ idx, float* __restrict__ w) {
+    constexpr int kPerLane = PL;
     const int lane = threadIdx.x & 63;
     for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += (int64_t)gridDim.x * 4) {
         const float* row = logits + t * E;
@@ -236,8 +238,12 @@ extern "C" int dwdp_route_topk(const void* x, const void* w_router, int in_dtype
         int rc = router_gemm(x, w_router, in_dtype, bias, T, H, E, logits_out, st);
         if (rc != DWDP_OK) return rc;
     }
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)std::min<int64_t>((T + 3) / 4, kMaxRowGrid)), dim3(256), 0, st,
-                       logits_out, T, E, k, topk_idx, topk_w);
+    const dim3 tgrid((unsigned)std::min<int64_t>((T + 3) / 4, kMaxRowGrid));
+    if (E <= 64) hipLaunchKernelGGL(topk_kernel<1>, tgrid, dim3(256), 0, st, logits_out, T, E, k, topk_idx, topk_w);
+    else if (E <= 128) hipLaunchKernelGGL(topk_kernel<2>, tgrid, dim3(256), 0, st, logits_out, T, E, k, topk_idx, topk_w);
+    else if (E <= 256) hipLaunchKernelGGL(topk_kernel<4>, tgrid, dim3(256), 0, st, logits_out, T, E, k, topk_idx, topk_w);
+    else if (E <= 512) hipLaunchKernelGGL(topk_kernel<8>, tgrid, dim3(256), 0, st, logits_out, T, E, k, topk_idx, topk_w);
+    else hipLaunchKernelGGL(topk_kernel<kMaxE / 64>, tgrid, dim3(256), 0, st, logits_out, T, E, k, topk_idx, topk_w);
     DWDP_LAUNCHED();
     return DWDP_OK;
 }
