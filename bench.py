@@ -189,6 +189,16 @@ def tile_trace(cfg, warm=3):
             if m.sum() == 32:
                 spread.append(float(st[m].max() - st[m].min()))
         q = lambda a: [round(float(np.percentile(a, x)), 1) for x in (10, 50, 90)] if len(a) else None
+        # per compute unit (XCD and HW_ID): the gap from one tile's end to the start of the next tile that
+        # unit takes (workgroup exit, dispatch of the next, its schedule lookup)
+        unit = tr["xcd"].astype(np.int64) * 256 + tr["hw_id"]
+        gaps, per_unit = [], []
+        for u in np.unique(unit):
+            m = np.nonzero(unit == u)[0]
+            o = m[np.argsort(st[m])]
+            per_unit.append(len(o))
+            gaps.extend((st[o[1:]] - en[o[:-1]]).tolist())
+        gaps = np.asarray(gaps)
         res[f"gemm{stage}"] = dict(
             tiles=int(len(tr)), span_us=round(span, 1),
             full_tile_us=round(float(dur[full].mean()), 1), full_tiles=int(full.sum()),
@@ -202,6 +212,9 @@ def tile_trace(cfg, warm=3):
                         for x in range(8)],
             xcd_is_workgroup_mod_8=round(float((tr["xcd"] == bid % 8).mean()), 4),
             cluster_start_spread_us_p10_50_90=q(spread),
+            compute_units=int(len(per_unit)), tiles_per_unit_min_max=[int(min(per_unit)), int(max(per_unit))],
+            inter_tile_gap_us_mean=round(float(gaps.mean()), 2) if len(gaps) else None,
+            inter_tile_gap_us_p10_50_90=q(gaps),
             single_mtile_group_tiles=int((tr["group_m_tiles"] == 1).sum()),
             rows_of_groups_traced=int(counts[np.unique(tr["group"])].sum()))
         log(f"GEMM{stage}: {res[f'gemm{stage}']}")

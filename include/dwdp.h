@@ -345,7 +345,8 @@ typedef struct {
     int32_t n_tile;             /* 256-column output tile (GEMM1: 128 gate + 128 up columns) */
     int32_t group_m_tiles;      /* m-tiles of the group */
     int32_t xcd;                /* XCD the workgroup ran on */
-    int32_t reserved_;
+    int32_t hw_id;              /* its compute unit inside the XCD: bits 15:8 of the HW_ID hardware
+                                   register (CU, shader array and shader engine numbers) */
 } dwdp_tile_record;
 
 /* Zero the trace array on the current device (stream ordered). */

@@ -35,7 +35,7 @@ class TileRecord(ctypes.Structure):
     _fields_ = [("t_start", ctypes.c_uint64), ("t_end", ctypes.c_uint64), ("order", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("first_row", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("n_tile", ctypes.c_int32), ("group_m_tiles", ctypes.c_int32), ("xcd", ctypes.c_int32),
-                ("reserved_", ctypes.c_int32)]
+                ("hw_id", ctypes.c_int32)]
 
 
 class DwdpError(RuntimeError):

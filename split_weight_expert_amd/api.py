@@ -223,6 +223,6 @@ def diag_tile_trace_read(max_records=1 << 17):
     _lib.check(_lib.load().dwdp_diag_tile_trace_read(buf, max_records, ctypes.byref(n)))
     dt = np.dtype([("t_start", "<u8"), ("t_end", "<u8"), ("order", "<i4"), ("group", "<i4"), ("first_row", "<i4"),
                    ("rows", "<i4"), ("n_tile", "<i4"), ("group_m_tiles", "<i4"), ("xcd", "<i4"),
-                   ("reserved_", "<i4")])
+                   ("hw_id", "<i4")])
     assert dt.itemsize == ctypes.sizeof(_lib.TileRecord)
     return np.frombuffer(bytes(buf)[: n.value * dt.itemsize], dtype=dt).copy()

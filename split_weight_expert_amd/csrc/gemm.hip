@@ -1319,7 +1319,7 @@ __global__ __launch_bounds__((FragCfg<BM, rowb_of(BM, FP8), FP8>::NW * 64), 1) v
         r.n_tile = c.t.nt;
         r.group_m_tiles = c.t.mc;
         r.xcd = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xF);   // hardware register XCC_ID, bits 3:0
-        r.reserved_ = 0;
+        r.hw_id = (int)((__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 8) & 0xFF);   // HW_ID bits 15:8
         tile_trace[blockIdx.x] = r;
     }
 #endif

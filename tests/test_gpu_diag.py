@@ -224,5 +224,8 @@ def test_tile_trace_full_size_schedules_cover_every_tile_once(name):
     for stage, n_tiles in ((1, I // 128), (2, H // 256)):
         _coverage(traces[stage], counts, n_tiles)
         assert ((traces[stage]["xcd"] >= 0) & (traces[stage]["xcd"] < 8)).all()
+        # thousands of tiles reach every one of the 256 compute units, each named once by (XCD, HW_ID)
+        units = np.unique(traces[stage]["xcd"].astype(np.int64) * 256 + traces[stage]["hw_id"])
+        assert len(units) == 256, f"stage {stage}: {len(units)} distinct compute units"
     del store, table, x, ws, y
     torch.cuda.empty_cache()
