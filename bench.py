@@ -8,7 +8,7 @@ buffers, combine -- on one batch already resident in HBM.  The layer-ahead
 prefetch runs on a side stream and is measured separately (copy alone, and
 its slowdown of the block when both run at once).
 
-Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  --gpus N with N > 1 exits: the library runs one rank on one GPU.
 """
 from __future__ import annotations
 
@@ -368,8 +368,8 @@ def roofline(cfg, g1_ms, rows, touched, peak):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU (asked for {args.gpus}); the multi-GPU layout is "
-              "described in DESIGN.md but not built", file=sys.stderr)
+        print(f"bench.py: the library runs one rank on one GPU (asked for {args.gpus} GPUs); runs across "
+              "several GPUs are not implemented", file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate_copy:
