@@ -63,6 +63,7 @@ ROUTE_CASES = [
     ("prefill8k_bf16", dict(T=130, H=512, E=1024, k=32)),   # the largest E and k the router takes
     ("prefill8k_bf16", dict(T=37, H=576, E=200, k=8)),      # 18 K steps over 16 waves, ragged T and E
     ("prefill8k_bf16", dict(T=2100, H=512, E=1000, k=8)),   # over 512 router tiles, ragged T and E
+    ("prefill8k_bf16", dict(T=300, H=512, E=200, k=6)),     # the DMA-ring router with ragged T and E
     ("tiny_f32", dict(T=70, E=1024, k=1)),
 ]
 
