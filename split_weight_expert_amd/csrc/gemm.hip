@@ -44,6 +44,9 @@
 // applied in the fold, so the MFMA itself must not scale: with code 0 the compiler emits the unscaled
 // v_mfma_f32_32x32x64_f8f6f4 (8 bytes shorter than the scaled form; 16K fp8 block 0.5% faster), with 127
 // (2^0) the scaled form with unit scales.  Both give the same products.
+#ifndef DWDP_FP8_GEMM2_BM256
+#define DWDP_FP8_GEMM2_BM256 1
+#endif
 #ifndef DWDP_ROUTER_DMA
 #define DWDP_ROUTER_DMA 1
 #endif
@@ -1487,9 +1490,12 @@ void launch_dma(const GemmParams& p, int64_t tiles, hipStream_t st) {
     hipLaunchKernelGGL((gemm_frag_kernel<BM, KIND, FP8>), dim3((unsigned)xcd_grid(tiles)), dim3(threads), 0, st, p);
 }
 
+// g2_wide (fp8, 128-row GEMM1 tiles): GEMM2 runs 256-row tiles, whose schedule replaces GEMM1's in the
+// same tables once GEMM1 is done (so a GEMM2-only call builds it too); maxm_wide bounds their m-tiles.
 template <int BM>
-void launch_ffn(bool g1, bool g2, bool fp8_path, const int32_t* offsets, int G, const GemmParams& p1,
-                const GemmParams& p2, MTile* mt_group, MTile* mt_size, int64_t maxm, hipStream_t st) {
+void launch_ffn(bool g1, bool g2, bool fp8_path, bool g2_wide, const int32_t* offsets, int G, const GemmParams& p1,
+                const GemmParams& p2, MTile* mt_group, MTile* mt_size, int64_t maxm, int64_t maxm_wide,
+                hipStream_t st) {
     if (g1) launch_schedule<BM>(offsets, G, const_cast<int32_t*>(p1.mprefix), mt_group, mt_size, p1.ticket, st);
 #ifdef DWDP_FP8_BM256
     constexpr bool fp8_tiles = true;
@@ -1499,7 +1505,17 @@ void launch_ffn(bool g1, bool g2, bool fp8_path, const int32_t* offsets, int G, 
     if constexpr (fp8_tiles) {
         if (fp8_path) {
             if (g1) launch_dma<BM, kGemm1, true>(p1, maxm * p1.NT, st);
-            if (g2) launch_dma<BM, kGemm2, true>(p2, maxm * p2.NT, st);
+            if (g2) {
+                if constexpr (BM == 128) {
+                    if (g2_wide) {
+                        launch_schedule<256>(offsets, G, const_cast<int32_t*>(p2.mprefix), mt_group, mt_size, nullptr,
+                                             st);
+                        launch_dma<256, kGemm2, true>(p2, maxm_wide * p2.NT, st);
+                        return;
+                    }
+                }
+                launch_dma<BM, kGemm2, true>(p2, maxm * p2.NT, st);
+            }
             return;
         }
     }
@@ -1630,10 +1646,18 @@ int grouped_ffn(int stage, const dwdp_expert_ptrs* table, int n_groups, const in
         if (g2) launch_f32<kGemm2>(p2, maxm * p2.NT, st);
     } else {
         const bool fp8 = w_dtype == DWDP_FP8_E4M3;
-        if (bm == 256) launch_ffn<256>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
-        else if (bm == 128) launch_ffn<128>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
-        else if (bm == 64) launch_ffn<64>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
-        else launch_ffn<32>(g1, g2, fp8, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, st);
+        // fp8 GEMM2 in 256-row tiles where the groups average 192 rows or more (the bf16 rule): half the
+        // weight re-reads of 128-row tiles; GEMM1 stays at 128 rows (its per-block rescale made 256-row
+        // tiles slower there)
+        const bool g2_wide = DWDP_FP8_GEMM2_BM256 && fp8 && bm == 128 && rows / n_groups >= 192;
+        const int64_t maxm_wide = (rows + 255) / 256 + n_groups;
+        if (bm == 256)
+            launch_ffn<256>(g1, g2, fp8, false, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, maxm, st);
+        else if (bm == 128)
+            launch_ffn<128>(g1, g2, fp8, g2_wide, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, maxm_wide, st);
+        else if (bm == 64)
+            launch_ffn<64>(g1, g2, fp8, false, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, maxm, st);
+        else launch_ffn<32>(g1, g2, fp8, false, offsets, n_groups, p1, p2, mt_group, mt_size, maxm, maxm, st);
     }
     DWDP_LAUNCHED();
     return DWDP_OK;

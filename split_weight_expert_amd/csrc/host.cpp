@@ -177,6 +177,9 @@ const char* dwdp_version(void) {
 #ifdef DWDP_MFMA_E8M0
            " mfma-e8m0=" DWDP_STR(DWDP_MFMA_E8M0)
 #endif
+#ifdef DWDP_FP8_GEMM2_BM256
+           " fp8-gemm2-bm256=" DWDP_STR(DWDP_FP8_GEMM2_BM256)
+#endif
 #ifdef DWDP_SILU_RCP
            " silu-rcp=" DWDP_STR(DWDP_SILU_RCP)
 #endif
